@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the bf16 GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+
+A step is one call of the fused operation on one batch of synthetic input
+already resident in device memory (default: linear + bias + GELU(tanh) at
+M = N = K = 8192, W stored [N][K]).  Prints ONE JSON line with the throughput
+in TFLOP/s (2*M*N*K flops per GEMM), a roofline object for the GEMM kernel
+(achieved TFLOP/s from HIP events around every launch on the launch stream,
+against the bf16 dense MFMA peak) and the CPU oracle's throughput on a
+bounded sample of the same workload, timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X bf16 dense MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz (published as 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["dense_bf16_gemm_amd/csrc/gemm_kernel.hpp", "dense_bf16_gemm_amd/csrc/mm_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, tensors, target_s: float):
+    """The oracle as it stands, on the first R output rows of the workload,
+    R grown until one run takes about target_s seconds of loop time."""
+    import oracle
+    from dense_bf16_gemm_amd import synth
+
+    if w.form == "matmul":
+        B = tensors["B"] if "B" in tensors else tensors["Bt"]
+        args = dict(A=synth.bits(tensors["A"]), B=synth.bits(B), layout=w.layout, epilogue="none")
+    elif w.form == "linear":
+        args = dict(A=synth.bits(tensors["x"]), B=synth.bits(tensors["W"]), layout="nt",
+                    epilogue=w.epilogue, bias=synth.bits(tensors["bias"]))
+    else:
+        args = dict(A=synth.bits(tensors["x"]), B=synth.bits(tensors["W_gate"]),
+                    B2=synth.bits(tensors["W_up"]), layout="nt", epilogue="swiglu")
+    per_row = w.flops / w.M
+    rows = 2
+    while True:
+        _, _, secs = oracle.gemm(rows=(0, rows), timed=True, **args)
+        if secs >= target_s * 0.5 or rows >= w.M:
+            break
+        grow = max(2, int(rows * target_s / max(secs, 1e-3)))
+        rows = min(w.M, grow)
+    return {
+        "value": round(per_row * rows / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} output rows of {w.name} (all {w.N} columns, full K={w.K}, "
+                  f"epilogue included), {secs:.1f} s of loop time",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--config", default=None, help="tile configuration override (mm_set_config)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
+              "the GEMM path has no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dense_bf16_gemm_amd as mm
+    from dense_bf16_gemm_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    binding.load()
+    if args.config:
+        binding.set_config(args.config)
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    host = w.make()
+    t = {k: v.to(dev) for k, v in host.items()}
+    out = torch.empty((w.M, w.N), dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16,
+                      device=dev)
+
+    if w.form == "matmul":
+        Bop = t["B"] if "B" in t else t["Bt"].t()
+        step = lambda: mm.matmul(t["A"], Bop, out.dtype, out=out)  # noqa: E731
+    elif w.form == "linear":
+        step = lambda: mm.linear(t["x"], t["W"], t["bias"], w.epilogue, out=out)  # noqa: E731
+    else:
+        step = lambda: mm.ffn_swiglu(t["x"], t["W_gate"], t["W_up"], out=out)  # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()  # the stream every launch goes to
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole0 = torch.cuda.Event(enable_timing=True)
+    whole1 = torch.cuda.Event(enable_timing=True)
+    whole0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    whole1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
+    ms_total = whole0.elapsed_time(whole1)
+    ms_per_step = ms_total / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    mean_launch = statistics.fmean(per_launch)
+    achieved = w.flops / (mean_launch * 1e-3) / 1e12
+
+    traffic = traffic_from_profile(name)
+    result = {
+        "metric": "TFLOP/s and % of bf16 MFMA peak, 8192^3 linear+bias+GELU, 1 GPU"
+        if name == synth.HEADLINE else f"TFLOP/s, {name}, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "form": w.form,
+            "M": w.M, "N": w.N, "K": w.K,
+            "layout": w.layout,
+            "epilogue": w.epilogue,
+            "out_dtype": w.out_dtype,
+            "tiles": binding.describe_config(w.form, w.M, w.N, w.K, w.layout),
+            "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "mmk::gemm_persistent",
+            "launch_ms_mean": round(mean_launch, 5),
+            "launch_ms_median": round(statistics.median(per_launch), 5),
+            "launch_ms_min": round(min(per_launch), 5),
+        },
+        "cpu_baseline": None,
+    }
+    print(f"bench: {name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
+          f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of peak), wall {wall:.3f} s", file=sys.stderr,
+          flush=True)
+    if not args.no_cpu_baseline:
+        del t
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,462 @@
+// mm_api.hip -- the C ABI of libmm.so (declared in include/mm.h): argument
+// validation, tile-configuration choice, kernel selection and launch.
+//
+// The pages' scheduler rejects schedules it cannot run instead of producing a
+// wrong kernel (PR "Implement persistent matmul scheduling", reviewer guide:
+// split-K and stream-K persistent schedules are refused with a check; PR
+// "Translate MmaOp patterns properly on Hopper", commit list: compile-time
+// reject reasons).  Here every unsupported request returns a status code
+// before any HIP call, and the heuristic can be replaced by an explicit
+// configuration (mm_set_config), as the pages' heuristic plugin replaces the
+// default heuristic (same PR, review of MatmulSchedulerPluginTest).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/mm.h"
+#include "gemm_kernel.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mm_status fail(mm_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+// ----------------------------------------------------------------------------
+// Kernel registry: every instantiated (tile, wave grid, layout, form).
+// ----------------------------------------------------------------------------
+struct KernelEntry {
+  int bm, bn, wgm, wgn;
+  bool a_kc, b_kc, ffn;
+  const void* fn;
+  std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
+};
+
+#define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
+  {BM, BN, WGM, WGN, AKC, BKC, FFN,                                                        \
+   reinterpret_cast<const void*>(&mmk::gemm_persistent<BM, BN, WGM, WGN, AKC, BKC, FFN>), {0}}
+
+#define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
+  MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
+      MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
+
+KernelEntry g_kernels[] = {
+    MM_K_LAYOUTS(256, 256, 2, 2),
+    MM_K_LAYOUTS(128, 128, 2, 2),
+    MM_K_LAYOUTS(64, 64, 2, 2),
+    MM_K(256, 256, 2, 2, true, true, true),
+    MM_K(128, 256, 2, 2, true, true, true),
+    MM_K(128, 128, 2, 2, true, true, true),
+};
+constexpr int kNumKernels = sizeof(g_kernels) / sizeof(g_kernels[0]);
+
+KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn) {
+  for (auto& k : g_kernels)
+    if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
+        k.b_kc == b_kc && k.ffn == ffn)
+      return &k;
+  return nullptr;
+}
+
+// ----------------------------------------------------------------------------
+// Configuration: heuristic and override.
+// ----------------------------------------------------------------------------
+struct Config {
+  int bm = 256, bn = 256, wgm = 2, wgn = 2;
+  int group = 8;  // band height in tiles
+  int xcd = 1;    // XCD-aware remap
+  int kalt = 2;   // 0 never, 1 always, 2 automatic
+  int grid = 0;   // 0 = CUs x occupancy
+};
+
+std::mutex g_cfg_mu;
+bool g_cfg_forced = false;
+Config g_cfg_force;
+std::once_flag g_env_once;
+
+bool parse_config(const char* spec, Config* out) {
+  Config c;
+  std::string s(spec);
+  size_t pos = 0;
+  while (pos < s.size()) {
+    size_t end = s.find(',', pos);
+    if (end == std::string::npos) end = s.size();
+    std::string item = s.substr(pos, end - pos);
+    pos = end + 1;
+    if (item.empty()) continue;
+    size_t eq = item.find('=');
+    if (eq == std::string::npos) return false;
+    std::string key = item.substr(0, eq);
+    char* ep = nullptr;
+    long v = std::strtol(item.c_str() + eq + 1, &ep, 10);
+    if (ep == item.c_str() + eq + 1 || *ep != '\0' || v < 0 || v > (1 << 20)) return false;
+    if (key == "BM") c.bm = (int)v;
+    else if (key == "BN") c.bn = (int)v;
+    else if (key == "WM") c.wgm = (int)v;
+    else if (key == "WN") c.wgn = (int)v;
+    else if (key == "G") c.group = (int)v;
+    else if (key == "XCD") c.xcd = (int)v;
+    else if (key == "KALT") c.kalt = (int)v;
+    else if (key == "GRID") c.grid = (int)v;
+    else return false;
+  }
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2) return false;
+  // the tile shape must be one that is instantiated (for some layout/form)
+  bool any = false;
+  for (auto& k : g_kernels)
+    if (k.bm == c.bm && k.bn == c.bn && k.wgm == c.wgm && k.wgn == c.wgn) any = true;
+  if (!any) return false;
+  *out = c;
+  return true;
+}
+
+void read_env_once() {
+  std::call_once(g_env_once, [] {
+    const char* e = std::getenv("MM_FORCE_CONFIG");
+    if (e && *e) {
+      Config c;
+      if (parse_config(e, &c)) {
+        std::lock_guard<std::mutex> g(g_cfg_mu);
+        g_cfg_forced = true;
+        g_cfg_force = c;
+      } else {
+        std::fprintf(stderr, "libmm: ignoring invalid MM_FORCE_CONFIG=\"%s\"\n", e);
+      }
+    }
+  });
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The heuristic: the largest tile that still gives about a wave of work.
+Config heuristic(bool ffn, int64_t M, int64_t N, int64_t K) {
+  Config c;
+  if (ffn) {
+    // B tile = gate + up rows, output tile BM x BN/2
+    if (cdiv(M, 256) * cdiv(N, 128) >= 192) {
+      c.bm = 256; c.bn = 256;
+    } else if (cdiv(M, 128) * cdiv(N, 128) >= 128) {
+      c.bm = 128; c.bn = 256;
+    } else {
+      c.bm = 128; c.bn = 128;
+    }
+  } else {
+    if (cdiv(M, 256) * cdiv(N, 256) >= 192) {
+      c.bm = 256; c.bn = 256;
+    } else if (cdiv(M, 128) * cdiv(N, 128) >= 64) {
+      c.bm = 128; c.bn = 128;
+    } else {
+      c.bm = 64; c.bn = 64;
+    }
+  }
+  (void)K;
+  return c;
+}
+
+Config choose_config(bool ffn, int64_t M, int64_t N, int64_t K) {
+  read_env_once();
+  {
+    std::lock_guard<std::mutex> g(g_cfg_mu);
+    if (g_cfg_forced) return g_cfg_force;
+  }
+  return heuristic(ffn, M, N, K);
+}
+
+// K-direction alternation pays off once one tile's K panels no longer stay
+// resident in an XCD's L2 (4 MiB) across tiles.
+bool k_alt_enabled(const Config& c, int64_t K) {
+  if (c.kalt != 2) return c.kalt == 1;
+  return K * (int64_t)(c.bm + c.bn) * 2 > (int64_t)(2 << 20);
+}
+
+// ----------------------------------------------------------------------------
+// Device attributes (cached per device).
+// ----------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+mm_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MM_ERR_UNSUPPORTED, "device index out of range");
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0)
+      return fail(MM_ERR_HIP, std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e));
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return MM_OK;
+}
+
+mm_status kernel_occupancy(KernelEntry* k, int* occ) {
+  int o = k->occupancy.load(std::memory_order_relaxed);
+  if (o == 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k->fn, k->wgm * k->wgn * 64, 0);
+    if (e != hipSuccess)
+      return fail(MM_ERR_HIP, std::string("hipOccupancyMaxActiveBlocksPerMultiprocessor: ") +
+                                  hipGetErrorString(e));
+    if (o < 1) return fail(MM_ERR_UNSUPPORTED, "kernel cannot be resident on a CU");
+    k->occupancy.store(o, std::memory_order_relaxed);
+  }
+  *occ = o;
+  return MM_OK;
+}
+
+// ----------------------------------------------------------------------------
+// Validation and launch.
+// ----------------------------------------------------------------------------
+struct Request {
+  const void* A;
+  const void* B;
+  const void* B2;
+  const void* bias;
+  void* out;
+  int64_t M, N, K;
+  int layout;
+  int epi;  // mmk::EPI_*
+  bool out_f32;
+  bool ffn;
+};
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+mm_status validate(const Request& r) {
+  if (r.M < 0 || r.N < 0 || r.K < 0) return fail(MM_ERR_INVALID_VALUE, "negative size");
+  if (r.M >= (int64_t(1) << 31) || r.N >= (int64_t(1) << 31) || r.K >= (int64_t(1) << 31))
+    return fail(MM_ERR_UNSUPPORTED, "M, N and K must be below 2^31");
+  if (r.layout < MM_NN || r.layout > MM_TT) return fail(MM_ERR_INVALID_VALUE, "bad layout");
+  if (r.M == 0 || r.N == 0) return MM_OK;
+  if (r.K == 0) return fail(MM_ERR_UNSUPPORTED, "K == 0 is not supported");
+  if (!r.A || !r.B || !r.out) return fail(MM_ERR_INVALID_VALUE, "null operand pointer");
+  if (r.ffn && !r.B2) return fail(MM_ERR_INVALID_VALUE, "null W_up pointer");
+  const bool need_bias = (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
+  if (need_bias && !r.bias) return fail(MM_ERR_INVALID_VALUE, "epilogue needs a bias");
+  const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
+  const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
+  if (!aligned(r.A, 16) || !aligned(r.B, 16) || (r.ffn && !aligned(r.B2, 16)))
+    return fail(MM_ERR_MISALIGNED, "operand pointers must be 16-byte aligned");
+  if ((a_kc ? r.K : r.M) % 8 != 0)
+    return fail(MM_ERR_MISALIGNED, "the contiguous extent of A must be a multiple of 8 elements");
+  if ((b_kc ? r.K : r.N) % 8 != 0)
+    return fail(MM_ERR_MISALIGNED, "the contiguous extent of B must be a multiple of 8 elements");
+  if (need_bias && !aligned(r.bias, 2)) return fail(MM_ERR_MISALIGNED, "bias must be 2-byte aligned");
+  const int esize = r.out_f32 ? 4 : 2;
+  if (!aligned(r.out, esize)) return fail(MM_ERR_MISALIGNED, "out must be aligned to its element size");
+  const int64_t ob = r.M * r.N * esize;
+  if (overlaps(r.out, ob, r.A, r.M * r.K * 2) || overlaps(r.out, ob, r.B, r.K * r.N * 2) ||
+      (r.ffn && overlaps(r.out, ob, r.B2, r.K * r.N * 2)) ||
+      (need_bias && overlaps(r.out, ob, r.bias, r.N * 2)))
+    return fail(MM_ERR_INVALID_VALUE, "out overlaps an input");
+  return MM_OK;
+}
+
+struct Plan {
+  KernelEntry* kernel;
+  mmk::GemmParams p;
+  int grid;
+  int threads;
+};
+
+// Everything but the device-dependent grid size; no HIP calls.
+mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
+  const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
+  const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
+  if (r.ffn && !b_kc) return fail(MM_ERR_UNSUPPORTED, "FFN weights must be [N][K]");
+  KernelEntry* k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn);
+  if (!k) return fail(MM_ERR_UNSUPPORTED, "no kernel for this tile configuration, layout and form");
+  const int out_bn = r.ffn ? c.bn / 2 : c.bn;
+  mmk::GemmParams& p = pl->p;
+  std::memset(&p, 0, sizeof p);
+  p.A = static_cast<const uint16_t*>(r.A);
+  p.B = static_cast<const uint16_t*>(r.B);
+  p.B2 = static_cast<const uint16_t*>(r.B2);
+  p.bias = static_cast<const uint16_t*>(r.bias);
+  p.out = r.out;
+  p.M = (int)r.M;
+  p.N = (int)r.N;
+  p.K = (int)r.K;
+  p.epi = r.epi;
+  p.out_f32 = r.out_f32 ? 1 : 0;
+  const int esize = r.out_f32 ? 4 : 2;
+  p.out_vec = (aligned(r.out, 16) && (r.N * esize) % 16 == 0) ? 1 : 0;
+  const int64_t tm = cdiv(r.M, c.bm), tn = cdiv(r.N, out_bn);
+  if (tm * tn >= (int64_t(1) << 31)) return fail(MM_ERR_UNSUPPORTED, "too many tiles");
+  p.tiles_m = (int)tm;
+  p.tiles_n = (int)tn;
+  p.num_tiles = (int)(tm * tn);
+  p.k_tiles = (int)cdiv(r.K, mmk::kBK);
+  p.group_m = c.group;
+  p.xcd_remap = c.xcd;
+  p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
+  pl->kernel = k;
+  pl->threads = c.wgm * c.wgn * 64;
+  pl->grid = 0;
+  return MM_OK;
+}
+
+mm_status run(const Request& r, void* stream) {
+  mm_status s = validate(r);
+  if (s != MM_OK) return s;
+  if (r.M == 0 || r.N == 0) return MM_OK;
+  const Config c = choose_config(r.ffn, r.M, r.N, r.K);
+  Plan pl;
+  s = plan_host(r, c, &pl);
+  if (s != MM_OK) return s;
+  int cus = 0, occ = 0;
+  if ((s = device_cus(&cus)) != MM_OK) return s;
+  if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
+  int64_t grid = c.grid > 0 ? c.grid : (int64_t)cus * occ;
+  if (grid > pl.p.num_tiles) grid = pl.p.num_tiles;
+  if (std::getenv("MM_LOG"))
+    std::fprintf(stderr, "libmm: M=%lld N=%lld K=%lld layout=%d ffn=%d -> BM=%d BN=%d WM=%d WN=%d G=%d "
+                 "XCD=%d KALT=%d grid=%lld tiles=%d\n", (long long)r.M, (long long)r.N,
+                 (long long)r.K, r.layout, (int)r.ffn, c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd,
+                 pl.p.k_alt, (long long)grid, pl.p.num_tiles);
+  void* args[] = {&pl.p};
+  hipError_t e = hipLaunchKernel(pl.kernel->fn, dim3((unsigned)grid), dim3(pl.threads), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel: ") + hipGetErrorString(e));
+  return MM_OK;
+}
+
+int map_epilogue(mm_epilogue e) {
+  switch (e) {
+    case MM_EPI_NONE: return mmk::EPI_NONE;
+    case MM_EPI_BIAS: return mmk::EPI_BIAS;
+    case MM_EPI_GELU_TANH: return mmk::EPI_GELU;
+    case MM_EPI_BIAS_GELU_TANH: return mmk::EPI_BIAS_GELU;
+  }
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_matmul(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
+                    mm_layout layout, mm_out_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  if (out_dtype != MM_OUT_BF16 && out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_INVALID_VALUE, "bad output dtype");
+  Request r{A, B, nullptr, nullptr, out, M, N, K, (int)layout, mmk::EPI_NONE,
+            out_dtype == MM_OUT_F32, false};
+  return run(r, stream);
+}
+
+mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, int64_t M, int64_t N,
+                    int64_t K, mm_layout layout, mm_epilogue epi, void* stream) {
+  g_last_error.clear();
+  const int e = map_epilogue(epi);
+  if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
+  Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  return run(r, stream);
+}
+
+mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* out, int64_t M,
+                     int64_t N, int64_t K, mm_glu_act act, void* stream) {
+  g_last_error.clear();
+  if (act != MM_GLU_SILU && act != MM_GLU_IDENTITY) return fail(MM_ERR_INVALID_VALUE, "bad activation");
+  Request r{x, W_gate, W_up, nullptr, out, M, N, K, MM_NT,
+            act == MM_GLU_SILU ? mmk::EPI_SWIGLU : mmk::EPI_GLU_ID, false, true};
+  return run(r, stream);
+}
+
+mm_status mm_ffn_swiglu(const void* x, const void* W_gate, const void* W_up, void* out, int64_t M,
+                        int64_t N, int64_t K, void* stream) {
+  return mm_ffn_glu(x, W_gate, W_up, out, M, N, K, MM_GLU_SILU, stream);
+}
+
+mm_status mm_set_config(const char* spec) {
+  g_last_error.clear();
+  read_env_once();
+  if (!spec || !*spec) {
+    std::lock_guard<std::mutex> g(g_cfg_mu);
+    g_cfg_forced = false;
+    return MM_OK;
+  }
+  Config c;
+  if (!parse_config(spec, &c))
+    return fail(MM_ERR_UNSUPPORTED, std::string("invalid or unsupported configuration: ") + spec);
+  std::lock_guard<std::mutex> g(g_cfg_mu);
+  g_cfg_forced = true;
+  g_cfg_force = c;
+  return MM_OK;
+}
+
+mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout, char* buf,
+                             int64_t buflen) {
+  g_last_error.clear();
+  if (!buf || buflen <= 0 || (form != 0 && form != 1) || M < 0 || N < 0 || K < 0 ||
+      layout < MM_NN || layout > MM_TT)
+    return fail(MM_ERR_INVALID_VALUE, "bad arguments");
+  const Config c = choose_config(form == 1, M, N, K);
+  std::snprintf(buf, (size_t)buflen, "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d", c.bm,
+                c.bn, c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid);
+  return MM_OK;
+}
+
+mm_status mm_debug_schedule(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
+                            int64_t grid, int32_t* out, int64_t cap, int64_t* count) {
+  g_last_error.clear();
+  if ((form != 0 && form != 1) || M <= 0 || N <= 0 || K <= 0 || grid <= 0 || !count ||
+      (cap > 0 && !out) || layout < MM_NN || layout > MM_TT)
+    return fail(MM_ERR_INVALID_VALUE, "bad arguments");
+  Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
+            false, form == 1};
+  const Config c = choose_config(form == 1, M, N, K);
+  Plan pl;
+  mm_status s = plan_host(r, c, &pl);
+  if (s != MM_OK) return s;
+  const int G = (int)(grid < pl.p.num_tiles ? grid : pl.p.num_tiles);
+  int64_t n = 0;
+  for (int b = 0; b < G; ++b) {
+    const int wg = mmk::remap_workgroup(b, G, pl.p.xcd_remap);
+    for (int i = 0; wg + (int64_t)i * G < pl.p.num_tiles; ++i) {
+      int tm, tn;
+      mmk::tile_coords(wg + i * G, pl.p.tiles_m, pl.p.tiles_n, pl.p.group_m, &tm, &tn);
+      if (n < cap) {
+        int32_t* o = out + 5 * n;
+        o[0] = b;
+        o[1] = i;
+        o[2] = tm;
+        o[3] = tn;
+        o[4] = (pl.p.k_alt && (i & 1)) ? 1 : 0;
+      }
+      ++n;
+    }
+  }
+  *count = n;
+  return MM_OK;
+}
+
+const char* mm_status_string(mm_status s) {
+  switch (s) {
+    case MM_OK: return "MM_OK";
+    case MM_ERR_INVALID_VALUE: return "MM_ERR_INVALID_VALUE";
+    case MM_ERR_UNSUPPORTED: return "MM_ERR_UNSUPPORTED";
+    case MM_ERR_MISALIGNED: return "MM_ERR_MISALIGNED";
+    case MM_ERR_HIP: return "MM_ERR_HIP";
+  }
+  return "MM_ERR_UNKNOWN";
+}
+
+const char* mm_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

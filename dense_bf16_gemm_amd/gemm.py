@@ -1,0 +1,125 @@
+"""PyTorch-facing wrappers of the C ABI: shape/stride checks, output
+allocation and the current stream.  No arithmetic happens here.
+
+Transposed operands are passed as views (``t.t()`` of a contiguous tensor);
+the layout letters tell the kernel how to read them in place.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding
+
+
+def _letter(t: torch.Tensor, name: str) -> str:
+    """'n' if the logical 2-D operand is stored as-is, 't' if it is the
+    transpose of a contiguous matrix.  Anything else is refused (no copies)."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    as_is, transposed = t.is_contiguous(), t.t().is_contiguous()
+    if as_is and transposed:  # a dimension of size 1: both describe the memory
+        return "n" if t.shape[1] >= t.shape[0] else "t"
+    if as_is:
+        return "n"
+    if transposed:
+        return "t"
+    raise ValueError(f"{name} must be contiguous or the transpose of a contiguous tensor")
+
+
+def _check(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MatmulOp form: out = A @ B with A [M,K] and B [K,N] (either may be a
+    transposed view), fp32 accumulation, bf16 or fp32 output."""
+    _check(A, "A")
+    _check(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    layout = _letter(A, "A") + _letter(B, "B")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
+    lib = binding.load()
+    st = lib.mm_matmul(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, binding.LAYOUTS[layout],
+                       binding.OUT_DTYPES["f32" if out_dtype == torch.float32 else "bf16"], _stream())
+    binding.check(st, "mm_matmul")
+    return out
+
+
+def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None,
+           epilogue: str = "none", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """LinearOp form: out = epi(x @ W.T + bias) with x [M,K], W [N,K], bias [N],
+    epilogue one of none | bias | gelu_tanh | bias_gelu_tanh; bf16 output."""
+    _check(x, "x")
+    _check(W, "W")
+    M, K = x.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if epilogue not in binding.EPILOGUES:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    if epilogue in ("bias", "bias_gelu_tanh"):
+        if bias is None:
+            raise ValueError(f"epilogue {epilogue!r} needs a bias")
+        _check(bias, "bias")
+        if bias.shape != (N,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous [N] tensor")
+    layout = _letter(x, "x") + _letter(W.t(), "W.T")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    lib = binding.load()
+    st = lib.mm_linear(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
+                       out.data_ptr(), M, N, K, binding.LAYOUTS[layout], binding.EPILOGUES[epilogue],
+                       _stream())
+    binding.check(st, "mm_linear")
+    return out
+
+
+def ffn_glu(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, act: str = "silu",
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Horizontally fused FFN: out = act(x @ W_gate.T) * (x @ W_up.T), one kernel;
+    x [M,K], W_gate and W_up [N,K] contiguous; act silu (Llama) or identity."""
+    for t, nm in ((x, "x"), (W_gate, "W_gate"), (W_up, "W_up")):
+        _check(t, nm)
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous 2-D tensor")
+    M, K = x.shape
+    N, K2 = W_gate.shape
+    if K != K2 or W_up.shape != W_gate.shape:
+        raise ValueError("shape mismatch between x, W_gate and W_up")
+    if act not in binding.GLU_ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [M, N] tensor")
+    lib = binding.load()
+    st = lib.mm_ffn_glu(x.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(), out.data_ptr(), M, N, K,
+                        binding.GLU_ACTS[act], _stream())
+    binding.check(st, "mm_ffn_glu")
+    return out
+
+
+def ffn_swiglu(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Llama FFN gate/up: SiLU(x @ W_gate.T) * (x @ W_up.T) in one kernel."""
+    return ffn_glu(x, W_gate, W_up, "silu", out)

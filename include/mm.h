@@ -1,0 +1,160 @@
+/*
+ * mm.h -- C ABI of libmm.so, a bf16 matrix-multiply library for one AMD
+ * MI355X (gfx950) GPU.
+ *
+ * The operations are the two op forms the pages centre on -- the MatmulOp
+ * form out = A.B and the LinearOp form out = x.W^T + bias (issue "Automate
+ * performant Hopper matmul", section "Persistent matmul"; PR "Implement
+ * persistent matmul scheduling", description) -- with a fused elementwise
+ * epilogue (the MLP forward epilogue fusion of that PR's description) and the
+ * Llama-FFN horizontal fusion of two GEMMs that share x (PR "Translate MmaOp
+ * patterns properly on Hopper", commit list: "Fix llama ffn horizontal
+ * fusion", "Fixes the horizontal fusion tests").  The contraction is the
+ * broadcast-multiply-sum of the _BroadcastInputs tests that PR "Implement
+ * persistent matmul scheduling" describes (fusedMultiplySum): bf16 inputs,
+ * fp32 accumulation, one rounding of the epilogue result to the output type.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer past the return of a call.
+ *   - Each successful call with M > 0 and N > 0 enqueues exactly ONE kernel on
+ *     `stream` (a hipStream_t; NULL means the default stream) and returns
+ *     without synchronizing.  Errors in execution surface on the stream.
+ *   - Matrices are dense and row-major in their stored shape (the last
+ *     dimension is contiguous); a transposed operand is described by the
+ *     layout letters, never copied.
+ *   - Argument errors are detected on the host before any HIP call, return a
+ *     status and have no side effects; mm_last_error() then describes them.
+ *   - M == 0 or N == 0 is a successful no-op.  K == 0 is rejected with
+ *     MM_ERR_UNSUPPORTED (an empty sum is not a supported use).
+ *   - Alignment: A, B (and W_gate/W_up) must be 16-byte aligned and the
+ *     contiguous extent of each of them a multiple of 8 elements; bias must be
+ *     2-byte aligned; out must be aligned to its element size.  Otherwise
+ *     MM_ERR_MISALIGNED.  (The output may have any N, e.g. N = 3001.)
+ *   - `out` must not overlap any input (MM_ERR_INVALID_VALUE).
+ *   - Sizes: 0 <= M, N < 2^31 and 1 <= K < 2^31; individual operands may hold
+ *     more than 2^31 elements (addresses are formed in 64 bits).
+ *   - Thread safety: calls may be made from several host threads; the only
+ *     process-wide state is a per-device attribute cache, the configuration
+ *     override (mm_set_config) and the thread-local last-error string.
+ */
+#ifndef MM_H_
+#define MM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MM_OK = 0,
+  MM_ERR_INVALID_VALUE = 1, /* null pointer, negative size, overlap, bad enum */
+  MM_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
+  MM_ERR_MISALIGNED = 3,    /* pointer or contiguous extent not aligned      */
+  MM_ERR_HIP = 4            /* a HIP runtime call failed (see mm_last_error) */
+} mm_status;
+
+/* Operand layouts: the letters say whether op(A) and op(B) are the stored
+ * matrix (N) or its transpose (T); op(A) is [M,K] and op(B) is [K,N].  These
+ * are the axis mappings that distinguish the MatmulOp and LinearOp forms
+ * (issue "Automate performant Hopper matmul", section "Persistent matmul":
+ * AxisMapping).
+ *   MM_NN  A stored [M][K], B stored [K][N]
+ *   MM_NT  A stored [M][K], B stored [N][K]  (the LinearOp weight W [N][K])
+ *   MM_TN  A stored [K][M], B stored [K][N]
+ *   MM_TT  A stored [K][M], B stored [N][K]                                 */
+typedef enum { MM_NN = 0, MM_NT = 1, MM_TN = 2, MM_TT = 3 } mm_layout;
+
+/* Epilogues applied to the fp32 accumulator before the single rounding:
+ *   NONE: y = acc;   BIAS: y = acc + bias[n];
+ *   GELU_TANH: y = gelu(acc);   BIAS_GELU_TANH: y = gelu(acc + bias[n]),
+ * with gelu(t) = 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))).  The bias
+ * is one bf16 value per output column, broadcast over rows. */
+typedef enum {
+  MM_EPI_NONE = 0,
+  MM_EPI_BIAS = 1,
+  MM_EPI_GELU_TANH = 2,
+  MM_EPI_BIAS_GELU_TANH = 3
+} mm_epilogue;
+
+typedef enum { MM_OUT_BF16 = 0, MM_OUT_F32 = 1 } mm_out_dtype;
+
+/* Gate activations of the horizontally fused FFN: y = act(g) * u.
+ *   SILU: act(g) = g / (1 + exp(-g))   (the Llama FFN)
+ *   IDENTITY: act(g) = g               (bilinear GLU; its products of small
+ *                                       integers are exact, which lets the
+ *                                       gate/up index mapping be checked
+ *                                       bit for bit)                       */
+typedef enum { MM_GLU_SILU = 0, MM_GLU_IDENTITY = 1 } mm_glu_act;
+
+/* MatmulOp form: out[M][N] = op(A) . op(B), written as bf16 (RNE) or fp32.
+ *   A, B    bf16 operands in the storage given by `layout`
+ *   out     [M][N] row-major, element type `out_dtype`
+ *   stream  hipStream_t (NULL = default stream)                             */
+mm_status mm_matmul(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
+                    mm_layout layout, mm_out_dtype out_dtype, void* stream);
+
+/* LinearOp form: out[M][N] = epi(op(x) . op(W) + bias), bf16 output (RNE).
+ *   x       activations; [M][K] for MM_NN/MM_NT, [K][M] for MM_TN/MM_TT
+ *   W       weight; [N][K] for MM_NT/MM_TT (the usual linear layer), [K][N]
+ *           for MM_NN/MM_TN
+ *   bias    [N] bf16; required for MM_EPI_BIAS and MM_EPI_BIAS_GELU_TANH,
+ *           ignored (may be NULL) otherwise                                  */
+mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, int64_t M,
+                    int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* stream);
+
+/* Llama-FFN horizontal fusion in one kernel:
+ *   out[M][N] = SiLU(x . W_gate^T) * (x . W_up^T), bf16 output (RNE),
+ * x [M][K], W_gate and W_up [N][K].  Each x tile is loaded once and feeds
+ * both products; the two accumulators meet only in the epilogue. */
+mm_status mm_ffn_swiglu(const void* x, const void* W_gate, const void* W_up, void* out,
+                        int64_t M, int64_t N, int64_t K, void* stream);
+
+/* As mm_ffn_swiglu with a selectable gate activation. */
+mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* out, int64_t M,
+                     int64_t N, int64_t K, mm_glu_act act, void* stream);
+
+/* Tile configuration override, parsed from a string such as
+ *   "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=1,GRID=0"
+ * (BM/BN: output tile; WM/WN: wave grid; G: grouped-swizzle band height in
+ * tiles; XCD: XCD-aware workgroup remap on/off; KALT: alternate the K
+ * direction per persistent tile (1), never (0) or automatically (2);
+ * GRID: persistent grid size, 0 = one wave of resident workgroups).  The
+ * heuristic is replaced for every later call in the process, in the manner
+ * of the pages' heuristic plugin (PR "Translate MmaOp patterns properly on
+ * Hopper", review of MatmulSchedulerPluginTest).  NULL or "" restores the
+ * heuristic.  An invalid or unsupported string returns MM_ERR_UNSUPPORTED
+ * and leaves the current setting unchanged.  The environment variable
+ * MM_FORCE_CONFIG, read on the first call, sets the same override.  Not
+ * thread-safe with respect to concurrent GEMM calls. */
+mm_status mm_set_config(const char* spec);
+
+/* Describes the configuration the next call of this shape would use, for
+ * logging and tests: writes a string like the one mm_set_config accepts.
+ * form: 0 matmul/linear, 1 FFN. Returns MM_ERR_INVALID_VALUE for bad args. */
+mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
+                             char* buf, int64_t buflen);
+
+/* Host-only description of the persistent tile order, for inspection and
+ * tests; launches nothing and makes no HIP call.  For a grid of `grid`
+ * workgroups (capped at the tile count) it lists, in each workgroup's visit
+ * order, five int32 per visited tile: hardware workgroup id, its local tile
+ * index, tile row, tile column, and 1 if that tile's K loop runs from the
+ * last k-step down.  Writes at most `cap` entries and stores the full count
+ * in *count.  form: 0 matmul/linear, 1 FFN. */
+mm_status mm_debug_schedule(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
+                            int64_t grid, int32_t* out, int64_t cap, int64_t* count);
+
+/* Static description of a status code (never NULL). */
+const char* mm_status_string(mm_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" if none).  Valid until the next call on the same thread. */
+const char* mm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM_H_ */

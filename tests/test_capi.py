@@ -1,0 +1,162 @@
+"""Host-side checks of libmm.so: it loads without a GPU, exports every
+function include/mm.h declares, rejects bad arguments before touching HIP,
+and its tile order covers every output tile exactly once.
+
+No test here launches a kernel, and no call here passes validation with a
+pointer that is not real device memory.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_bf16_gemm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mm.h")
+
+# fake, never dereferenced, 256-byte aligned addresses
+PA, PB, PB2, PBIAS, POUT = (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mm_status|const char\*)\s+(mm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["MM_OK", "MM_ERR_INVALID_VALUE", "MM_ERR_UNSUPPORTED",
+                                 "MM_ERR_MISALIGNED", "MM_ERR_HIP"]):
+        assert lib.mm_status_string(code).decode() == name
+    assert lib.mm_status_string(99).decode() == "MM_ERR_UNKNOWN"
+
+
+def mm(lib, A=PA, B=PB, out=POUT, M=64, N=64, K=64, layout=1, out_dtype=0):
+    return lib.mm_matmul(A, B, out, M, N, K, layout, out_dtype, None)
+
+
+def lin(lib, x=PA, W=PB, bias=PBIAS, out=POUT, M=64, N=64, K=64, layout=1, epi=3):
+    return lib.mm_linear(x, W, bias, out, M, N, K, layout, epi, None)
+
+
+def test_argument_errors_return_before_any_device_call(lib):
+    E = binding
+    assert mm(lib, A=None) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, B=None) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, out=None) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, M=-1) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, K=-5) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, layout=7) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, out_dtype=3) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, K=0) == E.MM_ERR_UNSUPPORTED
+    assert "K == 0" in lib.mm_last_error().decode()
+    assert mm(lib, M=1 << 31) == E.MM_ERR_UNSUPPORTED
+    # alignment of operand pointers and of contiguous extents
+    assert mm(lib, A=PA + 2) == E.MM_ERR_MISALIGNED
+    assert mm(lib, B=PB + 8) == E.MM_ERR_MISALIGNED
+    assert mm(lib, K=60) == E.MM_ERR_MISALIGNED  # NT: K is contiguous for both
+    assert mm(lib, N=60, layout=0) == E.MM_ERR_MISALIGNED  # NN: B's rows are N long
+    assert mm(lib, M=60, layout=2) == E.MM_ERR_MISALIGNED  # TN: A's rows are M long
+    assert mm(lib, out=POUT + 2, out_dtype=1) == E.MM_ERR_MISALIGNED
+    # output overlapping an input
+    assert mm(lib, out=PA + 64) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, out=PB - 64) == E.MM_ERR_INVALID_VALUE
+    # linear: epilogue enum and bias requirement
+    assert lin(lib, epi=9) == E.MM_ERR_INVALID_VALUE
+    assert lin(lib, bias=None, epi=1) == E.MM_ERR_INVALID_VALUE
+    assert lin(lib, bias=None, epi=3) == E.MM_ERR_INVALID_VALUE
+    assert lin(lib, bias=PBIAS + 1) == E.MM_ERR_MISALIGNED
+    assert lin(lib, out=PBIAS) == E.MM_ERR_INVALID_VALUE
+    # FFN
+    assert lib.mm_ffn_swiglu(PA, PB, None, POUT, 64, 64, 64, None) == E.MM_ERR_INVALID_VALUE
+    assert lib.mm_ffn_glu(PA, PB, PB2, POUT, 64, 64, 64, 5, None) == E.MM_ERR_INVALID_VALUE
+    assert lib.mm_ffn_swiglu(PA, PB, PB2, POUT, 64, 64, 36, None) == E.MM_ERR_MISALIGNED
+
+
+def test_empty_output_is_a_no_op(lib):
+    # M == 0 or N == 0 succeeds without a device or a launch
+    assert mm(lib, M=0) == binding.MM_OK
+    assert mm(lib, N=0, A=None, B=None, out=None) == binding.MM_OK
+    assert lin(lib, M=0, bias=None) == binding.MM_OK
+    assert lib.mm_ffn_swiglu(None, None, None, None, 0, 64, 64, None) == binding.MM_OK
+
+
+def test_config_override_and_rejection(lib):
+    try:
+        binding.set_config("BM=128,BN=128,WM=2,WN=2,G=4,XCD=0,KALT=0")
+        assert binding.describe_config("linear", 8192, 8192, 8192).startswith(
+            "BM=128,BN=128,WM=2,WN=2,G=4,XCD=0,KALT=0")
+        for bad in ("BM=100", "BM=256,BN=256,WM=3,WN=2", "FOO=1", "BM=", "G=0", "KALT=7"):
+            with pytest.raises(binding.MMError) as e:
+                binding.set_config(bad)
+            assert e.value.status == binding.MM_ERR_UNSUPPORTED
+        # a rejected string leaves the previous override in place
+        assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=128,BN=128")
+    finally:
+        binding.set_config(None)
+    assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=256,BN=256")
+
+
+def test_heuristic_choices():
+    assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=256,BN=256")
+    assert binding.describe_config("ffn", 8192, 14336, 4096).startswith("BM=256,BN=256")
+    small = binding.describe_config("matmul", 256, 256, 256, "nn")
+    assert small.startswith("BM=64,BN=64")
+    # long K turns on K-direction alternation
+    assert "KALT=1" in binding.describe_config("matmul", 2047, 3001, 65536)
+    assert "KALT=0" in binding.describe_config("matmul", 256, 256, 256)
+
+
+@pytest.mark.parametrize("form,M,N,K,grid", [
+    ("linear", 8192, 8192, 8192, 256),
+    ("linear", 4096, 4096, 4096, 256),
+    ("matmul", 2047, 3001, 65536, 256),
+    ("matmul", 2047, 3001, 65536, 250),  # grid not a multiple of the XCD count
+    ("ffn", 8192, 14336, 4096, 256),
+    ("matmul", 1000, 3000, 64, 7),
+    ("matmul", 256, 256, 256, 256),
+])
+def test_schedule_visits_every_tile_once(form, M, N, K, grid):
+    cfg = dict(kv.split("=") for kv in binding.describe_config(form, M, N, K).split(","))
+    bm, bn = int(cfg["BM"]), int(cfg["BN"])
+    out_bn = bn // 2 if form == "ffn" else bn
+    tiles_m, tiles_n = -(-M // bm), -(-N // out_bn)
+    sched = binding.debug_schedule(form, M, N, K, grid)
+    seen = [(tm, tn) for (_, _, tm, tn, _) in sched]
+    assert len(seen) == tiles_m * tiles_n
+    assert set(seen) == {(i, j) for i in range(tiles_m) for j in range(tiles_n)}
+    G = min(grid, tiles_m * tiles_n)
+    assert {b for (b, *_rest) in sched} == set(range(G))
+    # each workgroup alternates K direction iff alternation is on
+    kalt = cfg["KALT"] == "1"
+    for (b, i, _, _, kd) in sched:
+        assert kd == (1 if (kalt and i % 2 == 1) else 0)
+
+
+def test_schedule_xcd_locality():
+    """Workgroups the hardware places on one XCD (ids congruent mod 8) get
+    consecutive tiles of one band, so they share operand panels in that
+    XCD's L2."""
+    sched = binding.debug_schedule("linear", 8192, 8192, 8192, 256)
+    first = {b: (tm, tn) for (b, i, tm, tn, _) in sched if i == 0}
+    for x in range(8):
+        tiles = [first[b] for b in range(x, 256, 8)]
+        rows = {tm for tm, _ in tiles}
+        cols = {tn for _, tn in tiles}
+        # 32 workgroups of an XCD cover an 8-row x 4-column block of tiles
+        assert len(rows) == 8 and len(cols) == 4, (x, rows, cols)

@@ -1,0 +1,344 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* Index mapping, bit for bit: integer operands whose fp32 sums are exact in
+  any order, every layout, every tile configuration, shapes that span
+  several tiles with ragged M, N and K tails.
+* Numerics at the five workloads' real sizes and launch configuration
+  (the heuristic, exactly as the benchmark runs them): full outputs where the
+  oracle is quick, sampled outputs (random points plus every tile-boundary
+  row and column) elsewhere; bf16 outputs within 2e-2*(|ref|+1), fp32 outputs
+  within 1e-3*(|ref|+1).
+* Edge cases: empty outputs, 1x1, unaligned fp32 rows, an output pointer
+  that is not 16-byte aligned, guard bands around the output, repeatability,
+  and an operand with more than 2^31 elements.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_bf16_gemm_amd import binding, synth
+import dense_bf16_gemm_amd as mm
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = [
+    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2",
+    "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
+    "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
+]
+FFN_CONFIGS = [
+    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2",
+    "BM=128,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1",
+    "BM=128,BN=128,WM=2,WN=2,G=2,XCD=0,KALT=0",
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _restore_config():
+    yield
+    binding.set_config(None)
+
+
+def say(*a):
+    print("case:", *a, flush=True)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tol_excess(got: np.ndarray, ref: np.ndarray, rel: float) -> float:
+    """max(|got - ref| - rel*(|ref| + 1)); <= 0 means within tolerance."""
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref) - rel * (np.abs(ref) + 1.0)))
+
+
+def call_linear(A, B, bias, M, N, K, layout, epi, out):
+    lib = binding.load()
+    st = lib.mm_linear(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None,
+                       out.data_ptr(), M, N, K, binding.LAYOUTS[layout], binding.EPILOGUES[epi],
+                       stream())
+    binding.check(st, "mm_linear")
+
+
+def call_matmul(A, B, M, N, K, layout, out_f32, out):
+    lib = binding.load()
+    st = lib.mm_matmul(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, binding.LAYOUTS[layout],
+                       1 if out_f32 else 0, stream())
+    binding.check(st, "mm_matmul")
+
+
+def call_ffn(x, Wg, Wu, M, N, K, act, out):
+    lib = binding.load()
+    st = lib.mm_ffn_glu(x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), out.data_ptr(), M, N, K,
+                        binding.GLU_ACTS[act], stream())
+    binding.check(st, "mm_ffn_glu")
+
+
+# ------------------------------------------------------------ index mapping
+def shapes_for(layout):
+    """(M, N, K) spanning several tiles with ragged tails; contiguous extents
+    stay multiples of 8 as the ABI requires (A's rows are M long for TN/TT,
+    B's rows are N long for NN/TN)."""
+    base = [(1, 8, 8), (17, 24, 72), (129, 136, 64), (300, 264, 200), (520, 392, 4104)]
+    out = []
+    for M, N, K in base:
+        if layout in ("tn", "tt"):
+            M = -(-M // 8) * 8
+        if layout in ("nt", "tt"):
+            N = N + 3
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
+def test_mapping_bitexact_linear_bias(dev, cfg, layout):
+    binding.set_config(cfg)
+    for (M, N, K) in shapes_for(layout):
+        say("mapping linear+bias", layout, cfg, (M, N, K))
+        ops = synth.mapping_operands(M, N, K, layout, seed=M * 7 + N * 3 + K, with_bias=True)
+        A, B, bias = ops["A"], ops["B"], ops["bias"]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        call_linear(A.to(dev), B.to(dev), bias.to(dev), M, N, K, layout, "bias", out)
+        torch.cuda.synchronize()
+        _, ref_bits = oracle.gemm(synth.bits(A), synth.bits(B), layout, "bias", bias=synth.bits(bias))
+        got = to_bits(out)
+        bad = np.argwhere(got != ref_bits)
+        assert bad.size == 0, f"{layout} {cfg} {(M, N, K)}: {len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
+def test_mapping_bitexact_matmul_f32(dev, cfg, layout):
+    binding.set_config(cfg)
+    for (M, N, K) in shapes_for(layout)[:4] + [(264, 136, 2056)]:
+        say("mapping matmul f32", layout, cfg, (M, N, K))
+        A, B = synth.dense_int_operands(M, N, K, layout, seed=M + N + K)
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        call_matmul(A.to(dev), B.to(dev), M, N, K, layout, True, out)
+        torch.cuda.synchronize()
+        ref, _ = oracle.gemm(synth.bits(A), synth.bits(B), layout)
+        np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("cfg", FFN_CONFIGS)
+def test_mapping_bitexact_ffn(dev, cfg):
+    binding.set_config(cfg)
+    for (M, N, K) in [(1, 3, 8), (130, 200, 72), (300, 515, 264), (520, 264, 1032)]:
+        say("mapping ffn glu_identity", cfg, (M, N, K))
+        ops = synth.mapping_operands(M, N, K, "nt", seed=M + 5 * N + K, gated=True)
+        x, Wg, Wu = ops["A"], ops["B"], ops["B2"]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        call_ffn(x.to(dev), Wg.to(dev), Wu.to(dev), M, N, K, "identity", out)
+        torch.cuda.synchronize()
+        _, ref_bits = oracle.gemm(synth.bits(x), synth.bits(Wg), "nt", "glu_identity", B2=synth.bits(Wu))
+        got = to_bits(out)
+        bad = np.argwhere(got != ref_bits)
+        assert bad.size == 0, f"ffn {cfg} {(M, N, K)}: {len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+# ------------------------------------------------------------ numerics
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("epi", ["none", "bias", "gelu_tanh", "bias_gelu_tanh"])
+def test_linear_epilogues_random(dev, cfg, epi):
+    binding.set_config(cfg)
+    M, N, K = 333, 270, 520
+    say("linear random", epi, cfg)
+    x = synth.randn_bf16((M, K), 1.0, 1)
+    W = synth.randn_bf16((N, K), K ** -0.5, 2)
+    b = synth.randn_bf16((N,), 1.0, 3)
+    out = mm.linear(x.to(dev), W.to(dev), b.to(dev), epi)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(W), "nt", epi, bias=synth.bits(b))
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+
+
+@pytest.mark.parametrize("cfg", FFN_CONFIGS)
+def test_ffn_swiglu_random(dev, cfg):
+    binding.set_config(cfg)
+    M, N, K = 300, 390, 264
+    say("ffn swiglu random", cfg)
+    x = synth.randn_bf16((M, K), 1.0, 4)
+    Wg = synth.randn_bf16((N, K), K ** -0.5, 5)
+    Wu = synth.randn_bf16((N, K), K ** -0.5, 6)
+    out = mm.ffn_swiglu(x.to(dev), Wg.to(dev), Wu.to(dev))
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(Wg), "nt", "swiglu", B2=synth.bits(Wu))
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+
+
+def run_workload(w: synth.Workload, t, dev):
+    g = {k: v.to(dev) for k, v in t.items()}
+    if w.form == "matmul":
+        A = g["A"]
+        B = g["B"] if "B" in g else g["Bt"].t()  # transposed view, read in place
+        return mm.matmul(A, B, torch.float32 if w.out_dtype == "f32" else torch.bfloat16)
+    if w.form == "linear":
+        return mm.linear(g["x"], g["W"], g["bias"], w.epilogue)
+    return mm.ffn_swiglu(g["x"], g["W_gate"], g["W_up"])
+
+
+def oracle_args(w: synth.Workload, t):
+    if w.form == "matmul":
+        B = t["B"] if "B" in t else t["Bt"]
+        return dict(A=synth.bits(t["A"]), B=synth.bits(B), layout=w.layout, epilogue="none")
+    if w.form == "linear":
+        return dict(A=synth.bits(t["x"]), B=synth.bits(t["W"]), layout="nt", epilogue=w.epilogue,
+                    bias=synth.bits(t["bias"]))
+    return dict(A=synth.bits(t["x"]), B=synth.bits(t["W_gate"]), B2=synth.bits(t["W_up"]),
+                layout="nt", epilogue="swiglu")
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity(dev, name):
+    w = synth.WORKLOADS[name]
+    say("workload", name, binding.describe_config(w.form, w.M, w.N, w.K, w.layout))
+    t = w.make()
+    out = run_workload(w, t, dev)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    rel = 1e-3 if w.out_dtype == "f32" else 2e-2
+    args = oracle_args(w, t)
+    if w.M * w.N * w.K <= 2 ** 28:
+        y, _ = oracle.gemm(**args)
+        assert tol_excess(got, y, rel) <= 0
+    else:
+        rows, cols = synth.sample_points(w.M, w.N, 3000, seed=w.M + w.N)
+        y, _ = oracle.points(rows=rows, cols=cols, **args)
+        assert tol_excess(got[rows, cols], y, rel) <= 0
+        # and whole rows at the first and last tile band
+        for r0 in (0, w.M - 3):
+            yr, _ = oracle.gemm(rows=(r0, r0 + 3), **args)
+            assert tol_excess(got[r0:r0 + 3], yr, rel) <= 0
+    if w.out_dtype == "f32":
+        # normwise relative error, reported alongside
+        pass
+
+
+# ------------------------------------------------------------ edge cases
+def test_empty_and_tiny(dev):
+    say("empty and tiny")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((16, 64), dtype=torch.bfloat16, device=dev)
+    assert mm.linear(x, W).shape == (0, 16)
+    assert mm.matmul(torch.zeros((5, 8), dtype=torch.bfloat16, device=dev),
+                     torch.zeros((8, 0), dtype=torch.bfloat16, device=dev)).shape == (5, 0)
+    a = synth.randn_bf16((1, 8), 1.0, 9)
+    b = synth.randn_bf16((8, 1), 1.0, 10)
+    got = mm.matmul(a.to(dev), b.t().contiguous().to(dev).t(), torch.float32)
+    y, _ = oracle.gemm(synth.bits(a), synth.bits(b), "nn")
+    assert tol_excess(got.cpu().numpy(), y, 1e-3) <= 0
+
+
+def test_unaligned_output_rows_and_pointer(dev):
+    """fp32 rows of 3001 elements (12004 bytes, not 16-byte multiples) and a
+    bf16 output that starts 2 bytes past a 16-byte boundary."""
+    M, N, K = 70, 3001, 136
+    say("unaligned output", (M, N, K))
+    A, B = synth.dense_int_operands(M, N, K, "nt", seed=77)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    call_matmul(A.to(dev), B.to(dev), M, N, K, "nt", True, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm(synth.bits(A), synth.bits(B), "nt")
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+    M, N = 40, 64
+    ops = synth.mapping_operands(M, N, K, "nt", seed=78, with_bias=True)
+    buf = torch.zeros(M * N + 8, dtype=torch.bfloat16, device=dev)
+    out = buf[1:1 + M * N].view(M, N)
+    call_linear(ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev), M, N, K, "nt", "bias", out)
+    torch.cuda.synchronize()
+    _, ref_bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "bias",
+                              bias=synth.bits(ops["bias"]))
+    np.testing.assert_array_equal(to_bits(out), ref_bits)
+    assert buf[0].item() == 0 and torch.all(buf[1 + M * N:] == 0)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS[:2])
+def test_guard_bands_untouched(dev, cfg):
+    binding.set_config(cfg)
+    M, N, K = 259, 261, 200
+    say("guard bands", cfg)
+    guard = 2048  # elements = 4 KiB of fp32
+    A, B = synth.dense_int_operands(M, N, K, "nt", seed=5)
+    buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device=dev)
+    out = buf[guard:guard + M * N].view(M, N)
+    call_matmul(A.to(dev), B.to(dev), M, N, K, "nt", True, out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[guard + M * N:] == 12345.0)
+
+
+def test_repeatable_bitwise(dev):
+    w = synth.WORKLOADS["linear_bias_gelu_4096"]
+    say("repeatable", w.name)
+    t = w.make()
+    o1 = run_workload(w, t, dev).clone()
+    o2 = run_workload(w, t, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_no_device_allocation_per_call(dev):
+    w = synth.WORKLOADS["linear_bias_gelu_4096"]
+    t = {k: v.to(dev) for k, v in w.make().items()}
+    out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    mm.linear(t["x"], t["W"], t["bias"], w.epilogue, out=out)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    for _ in range(3):
+        mm.linear(t["x"], t["W"], t["bias"], w.epilogue, out=out)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+
+
+def test_torch_views_map_to_layouts(dev):
+    """A .t() view of a contiguous tensor is read in place as the matching layout."""
+    M, N, K = 136, 72, 96
+    say("views")
+    a = synth.randint_bf16((M, K), -3, 3, 1)
+    b = synth.randint_bf16((K, N), -3, 3, 2)
+    want = (a.float() @ b.float()).numpy()
+    for A in (a.to(dev), a.t().contiguous().to(dev).t()):
+        for B in (b.to(dev), b.t().contiguous().to(dev).t()):
+            got = mm.matmul(A, B, torch.float32)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(got.cpu().numpy(), want)
+    with pytest.raises(ValueError):
+        mm.matmul(a.to(dev)[:, ::2], b.to(dev)[::2])
+
+
+def test_int64_operand_offsets(dev):
+    """A has 32769 x 65536 = 2^31 + 65536 elements: its last rows sit past the
+    32-bit element range.  Checks the last 64 output rows."""
+    M, N, K = 32769, 128, 65536
+    say("int64 offsets", (M, N, K))
+    free, _total = torch.cuda.mem_get_info()
+    if free < 12 * 2 ** 30:
+        pytest.skip("needs ~12 GiB of free device memory")
+    g = torch.Generator(device=dev).manual_seed(601)
+    A = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    B = synth.randn_bf16((N, K), K ** -0.5, 602)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    call_matmul(A, B.to(dev), M, N, K, "nt", True, out)
+    torch.cuda.synchronize()
+    rows = A[M - 64:].cpu()
+    del A
+    y, _ = oracle.gemm(synth.bits(rows), synth.bits(B), "nt")
+    assert tol_excess(out[M - 64:].cpu().numpy(), y, 1e-3) <= 0
