@@ -102,15 +102,15 @@ __host__ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int
 // whose chunk lies past K, so a ragged last k-step arrives zero-filled.
 __device__ const u32x4 g_zero_chunk[1] = {{0u, 0u, 0u, 0u}};
 
-// XOR swizzle of the 16-byte chunk index by the LDS row.  Chosen (by an
-// exhaustive search over XOR-linear maps of the row bits) so that every
-// ds_read_b128 fragment pattern used below -- 16 consecutive rows, or the
-// 4x4-row comb of the permuted weight fragments -- touches distinct banks
-// whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle, while the
-// direct-to-LDS copies (8 lanes per 128-byte row) stay conflict free too.
-// It depends on row bits 0..4 only.
+// XOR swizzle of the 16-byte chunk index by the LDS row: chunk ^ (row & 7)
+// ^ (bit 4 of row moved to bit 2).  Chosen by measuring SQ_LDS_BANK_CONFLICT
+// for candidate XOR maps on the two ds_read_b128 fragment patterns used
+// below (16 consecutive rows; and the comb of 4 runs of 4 rows 8 apart used
+// by the permuted weight fragments): this one is conflict free on both, so a
+// 1 KiB fragment read takes the minimum 4 LDS cycles.  The direct-to-LDS
+// copies write whole rows and never conflict.  Depends on row bits 0..4 only.
 __host__ __device__ __forceinline__ int lds_swz(int row) {
-  return (row ^ (((row >> 3) & 1) * 5) ^ ((row >> 4) & 1)) & 7;
+  return (row ^ ((row >> 2) & 4)) & 7;
 }
 
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {

@@ -20,6 +20,7 @@
 
 #include "../../include/mm.h"
 #include "gemm_kernel.hpp"
+#include "gemm_nt_pipe.hpp"
 
 namespace {
 
@@ -36,19 +37,29 @@ mm_status fail(mm_status s, const std::string& msg) {
 struct KernelEntry {
   int bm, bn, wgm, wgn;
   bool a_kc, b_kc, ffn;
+  int pipe;  // 1: the 4-stage K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
   const void* fn;
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
 };
 
 #define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
-  {BM, BN, WGM, WGN, AKC, BKC, FFN,                                                        \
+  {BM, BN, WGM, WGN, AKC, BKC, FFN, 0,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_persistent<BM, BN, WGM, WGN, AKC, BKC, FFN>), {0}}
+
+#define MM_KP(BM, BN, WGM, WGN, FFN)                                                       \
+  {BM, BN, WGM, WGN, true, true, FFN, 1,                                                   \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_pipe<BM, BN, WGM, WGN, FFN>), {0}}
 
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
+    MM_KP(256, 256, 2, 2, false),
+    MM_KP(128, 128, 2, 2, false),
+    MM_KP(256, 256, 2, 2, true),
+    MM_KP(128, 256, 2, 2, true),
+    MM_KP(128, 128, 2, 2, true),
     MM_K_LAYOUTS(256, 256, 2, 2),
     MM_K_LAYOUTS(128, 128, 2, 2),
     MM_K_LAYOUTS(64, 64, 2, 2),
@@ -58,10 +69,10 @@ KernelEntry g_kernels[] = {
 };
 constexpr int kNumKernels = sizeof(g_kernels) / sizeof(g_kernels[0]);
 
-KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn) {
+KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe) {
   for (auto& k : g_kernels)
     if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
-        k.b_kc == b_kc && k.ffn == ffn)
+        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe)
       return &k;
   return nullptr;
 }
@@ -75,6 +86,7 @@ struct Config {
   int xcd = 1;    // XCD-aware remap
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
+  int pipe = 1;   // prefer the 4-stage K-contiguous pipeline where it exists
 };
 
 std::mutex g_cfg_mu;
@@ -106,9 +118,10 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "XCD") c.xcd = (int)v;
     else if (key == "KALT") c.kalt = (int)v;
     else if (key == "GRID") c.grid = (int)v;
+    else if (key == "PIPE") c.pipe = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 1) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -268,7 +281,7 @@ mm_status validate(const Request& r) {
 }
 
 struct Plan {
-  KernelEntry* kernel;
+  KernelEntry* kernel = nullptr;
   mmk::GemmParams p;
   int grid;
   int threads;
@@ -279,7 +292,12 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
   if (r.ffn && !b_kc) return fail(MM_ERR_UNSUPPORTED, "FFN weights must be [N][K]");
-  KernelEntry* k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn);
+  KernelEntry* k = nullptr;
+  // the pipelined kernel addresses a tile's rows with 32-bit buffer offsets
+  const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
+  if (c.pipe && span < (int64_t(1) << 31))
+    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, 1);
+  if (!k) k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, 0);
   if (!k) return fail(MM_ERR_UNSUPPORTED, "no kernel for this tile configuration, layout and form");
   const int out_bn = r.ffn ? c.bn / 2 : c.bn;
   mmk::GemmParams& p = pl->p;
@@ -301,7 +319,9 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   p.tiles_m = (int)tm;
   p.tiles_n = (int)tn;
   p.num_tiles = (int)(tm * tn);
-  p.k_tiles = (int)cdiv(r.K, mmk::kBK);
+  // the pipelined kernel runs k-steps of 32 in pairs: an even count, padded
+  // with k-steps past K that read zeros
+  p.k_tiles = k->pipe ? (int)(2 * cdiv(r.K, 2 * mmk::kPipeBK)) : (int)cdiv(r.K, mmk::kBK);
   p.group_m = c.group;
   p.xcd_remap = c.xcd;
   p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
@@ -407,8 +427,8 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
       layout < MM_NN || layout > MM_TT)
     return fail(MM_ERR_INVALID_VALUE, "bad arguments");
   const Config c = choose_config(form == 1, M, N, K);
-  std::snprintf(buf, (size_t)buflen, "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d", c.bm,
-                c.bn, c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid);
+  std::snprintf(buf, (size_t)buflen, "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d",
+                c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe);
   return MM_OK;
 }
 
