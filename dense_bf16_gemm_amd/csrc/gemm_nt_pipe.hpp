@@ -29,7 +29,7 @@ namespace mmk {
 
 constexpr int kPipeBK = 32;      // k per stage
 constexpr int kPipeRowB = 64;    // LDS bytes per row of a stage
-constexpr int kPipeStages = 4;
+constexpr int kPipeStages = 5;
 
 // Swizzle of 64-byte rows: chunk ^ (bit 3 of row) << 1, measured conflict
 // free (SQ_LDS_BANK_CONFLICT) for 16 consecutive rows and for the 4x4-row
@@ -57,7 +57,7 @@ gemm_nt_pipe(GemmParams p) {
   static_assert(LA >= 1 && LB >= 1 && (BM / 16) % NW == 0 && (BN / 16) % NW == 0, "copy split");
   static_assert(FN % 2 == 0 && (!FFN || FN % 4 == 0), "fragment pairs");
   static_assert(WTN % 32 == 0 && WTM % 16 == 0, "wave tile");
-  static_assert(2 * LOADS <= 63, "vmcnt range");
+  static_assert((kPipeStages - 1) * LOADS <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) char smem[kPipeStages * STAGE_BYTES];
 
@@ -88,42 +88,47 @@ gemm_nt_pipe(GemmParams p) {
   const uint32_t lane_base = (uint32_t)crow * row_bytes + 16u * (uint32_t)cchunk;
   constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 
-  auto kstep_of = [&](int tile_i, int kt) {
-    return (p.k_alt && (tile_i & 1)) ? (KT - 1 - kt) : kt;
-  };
-
-  // Issues the copies of one k-step (tile_i, kt) into the stage at byte
-  // offset `stage_off` of the LDS ring.
-  auto issue_copies = [&](int tile_i, int kt, int stage_off) {
+  // Per-tile copy state of the load cursor, set when the cursor enters a
+  // tile: buffer resources of the tile's A rows and weight rows, and the K
+  // direction.  Each k-step then costs a handful of instructions per copy.
+  __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+  int ld_alt = 0;
+  auto enter_tile = [&](int tile_i) {
     int tm, tn;
     tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-    const int k0 = kstep_of(tile_i, kt) * kPipeBK;
-    const uint32_t koff = lane_base + 2u * (uint32_t)k0 +
-                          ((k0 + 8 * cchunk) < K ? 0u : 0x80000000u);
     const int m0 = tm * BM;
     const int mrows = (M - m0) < BM ? (M - m0) : BM;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.A + (int64_t)m0 * ld), (short)0, (int)((uint32_t)mrows * row_bytes),
-        kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int j = i * NW + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(smem + stage_off + j * 1024), 16,
-          koff + (uint32_t)(16 * j) * row_bytes, 0, 0, 0);
-    }
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.A + (int64_t)m0 * ld), (short)0,
+                                           (int)((uint32_t)mrows * row_bytes), kRsrcWord3);
     const int n0 = tn * OUT_BN;
     const int nrows = (N - n0) < OUT_BN ? (N - n0) : OUT_BN;
     const int nrec = (int)((uint32_t)nrows * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.B + (int64_t)n0 * ld), (short)0, nrec, kRsrcWord3);
-    __amdgpu_buffer_rsrc_t rb1 = rb0;
+    rb0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B + (int64_t)n0 * ld), (short)0,
+                                            nrec, kRsrcWord3);
+    rb1 = rb0;
     if constexpr (FFN)
       rb1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B2 + (int64_t)n0 * ld),
                                               (short)0, nrec, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int j = i * NW + wave;
+    ld_alt = p.k_alt && (tile_i & 1);
+  };
+
+  // Lane offset of the copies of k-step kt of the cursor's tile: chunks past
+  // K are pushed out of range (top bit) and read as zero.
+  auto copy_koff = [&](int kt) {
+    const int k0 = (ld_alt ? (KT - 1 - kt) : kt) * kPipeBK;
+    return lane_base + 2u * (uint32_t)k0 + ((k0 + 8 * cchunk) < K ? 0u : 0x80000000u);
+  };
+
+  // Issues copy q (of LOADS) of one k-step into the stage at byte offset
+  // stage_off: copies 0..LA-1 fill A rows, the rest weight rows.
+  auto issue_copy = [&](int q, uint32_t koff, int stage_off) {
+    if (q < LA) {
+      const int j = q * NW + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(smem + stage_off + j * 1024), 16,
+          koff + (uint32_t)(16 * j) * row_bytes, 0, 0, 0);
+    } else {
+      const int j = (q - LA) * NW + wave;
       const int r0 = 16 * j;  // first B-tile row of this copy
       int prow = r0;          // its row within the weight panel
       bool up = false;
@@ -152,6 +157,15 @@ gemm_nt_pipe(GemmParams p) {
   bf16x8 fa[2][FM], fb[2][FN];
   f32x4 acc[FM][FN];
 
+  // Fragment f of a k-step: f < FN is weight fragment f, else A fragment f-FN.
+  auto read_frag = [&](const char* stage, int f, bf16x8* a, bf16x8* b) {
+    if (f < FN)
+      b[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                            stage + b_off + (32 * (f >> 1) + 4 * (f & 1)) * kPipeRowB));
+    else
+      a[f - FN] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                 stage + a_off + 16 * (f - FN) * kPipeRowB));
+  };
   auto read_frags = [&](const char* stage, bf16x8* a, bf16x8* b) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -163,17 +177,28 @@ gemm_nt_pipe(GemmParams p) {
                                              stage + a_off + 16 * fm * kPipeRowB));
   };
 
-  // ---- load cursor: the k-step whose copies are issued next.  Branch free,
-  // so the copies stay in the same scheduling region as the MFMAs.
-  int ld_tile = 0, ld_kt = 0;
-  auto issue_next = [&](int issued_index) {
-    // past the end: re-copy the last k-step (in bounds, never read)
-    const bool live = ld_tile < my_tiles;
-    issue_copies(live ? ld_tile : my_tiles - 1, live ? ld_kt : KT - 1,
-                 (issued_index % kPipeStages) * STAGE_BYTES);
-    const bool wrap = (ld_kt + 1 == KT);
-    ld_kt = wrap ? 0 : ld_kt + 1;
-    ld_tile = wrap ? ld_tile + 1 : ld_tile;
+  // ---- load cursor: (ld_tile, ld_kt) is the k-step whose copies are issued
+  // next; past the last k-step it keeps re-copying that k-step (in bounds,
+  // never read).  ld_stage is its ring slot.
+  int ld_tile = 0, ld_kt = 0, ld_stage = 0;
+  enter_tile(0);
+  // Advances the cursor; entering a new tile rebuilds the per-tile state.
+  // Kept out of the scheduling region of the MFMAs (it may branch).
+  auto advance_cursor = [&]() {
+    ld_stage = (ld_stage + 1 == kPipeStages) ? 0 : ld_stage + 1;
+    if (ld_tile < my_tiles) {
+      if (++ld_kt == KT) {
+        ld_kt = 0;
+        ++ld_tile;
+        if (ld_tile < my_tiles) enter_tile(ld_tile);
+        else ld_kt = KT - 1;  // stay on the last k-step
+      }
+    }
+  };
+  auto issue_next = [&]() {
+    const uint32_t koff = copy_koff(ld_kt);
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) issue_copy(q, koff, ld_stage * STAGE_BYTES);
   };
 
   // ---- prologue: k-steps 0..3 in flight; wait for k-step 0 and read its
@@ -181,44 +206,48 @@ gemm_nt_pipe(GemmParams p) {
   // it+2, it+3 are outstanding and the fragments of k-step it are in
   // registers.
 #pragma unroll
-  for (int s = 0; s < kPipeStages; ++s) issue_next(s);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * LOADS));
+  for (int s = 0; s < kPipeStages; ++s) {
+    issue_next();
+    advance_cursor();
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kPipeStages - 1) * LOADS));
   __builtin_amdgcn_s_barrier();
   read_frags(smem, fa[0], fb[0]);
 
   // One k-step: P = parity of the running counter (register set in use).
-  auto kstep = [&](auto par, int it) {
+  // rd_stage: the ring slot holding the k-step after the current one
+  int rd_stage = 1;
+  auto kstep = [&](auto par) {
     constexpr int P = decltype(par)::value;
     // own copies of k-step it+1 done, own fragment reads done; then all
     // waves: k-step it+1 is visible and stage it % 4 (whose data every wave
     // already holds in registers) is free for the copies of k-step it+4
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kPipeStages - 2) * LOADS));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_next(it + kPipeStages);
-    read_frags(smem + ((it + 1) % kPipeStages) * STAGE_BYTES, fa[P ^ 1], fb[P ^ 1]);
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[P][fn], fa[P][fm], acc[fm][fn], 0, 0, 0);
-    // interleave: copies and fragment reads spread between the MFMAs
+    // LOADS chunks of {one copy, a share of the next fragments, a share of
+    // the MFMAs}, fenced from each other: the copies and reads are spread
+    // evenly over the MFMAs.  Bunched copies overfill the vector-memory
+    // address queue, and a wave stalled on a copy cannot issue the MFMAs
+    // behind it.
     constexpr int NMFMA = FM * FN;
     constexpr int NDS = FM + FN;
-    constexpr int PER = NMFMA / (LOADS + NDS);
+    const uint32_t koff = copy_koff(ld_kt);
+    const char* rd = smem + rd_stage * STAGE_BYTES;
 #pragma unroll
-    for (int g = 0; g < LOADS; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (copy)
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // MFMA
-    }
+    for (int c = 0; c < LOADS; ++c) {
+      issue_copy(c, koff, ld_stage * STAGE_BYTES);
 #pragma unroll
-    for (int g = 0; g < NDS; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // MFMA
+      for (int f = (c * NDS) / LOADS; f < ((c + 1) * NDS) / LOADS; ++f) read_frag(rd, f, fa[P ^ 1], fb[P ^ 1]);
+#pragma unroll
+      for (int i = (c * NMFMA) / LOADS; i < ((c + 1) * NMFMA) / LOADS; ++i) {
+        const int fm = i / FN, fn = i % FN;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[P][fn], fa[P][fm], acc[fm][fn], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  int it = 0;
   for (int tile_i = 0; tile_i < my_tiles; ++tile_i) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -226,9 +255,13 @@ gemm_nt_pipe(GemmParams p) {
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // k-steps in pairs so each register set has a fixed role (the host makes
     // KT even: a padding k-step past K reads zeros)
-    for (int kt = 0; kt < KT; kt += 2, it += 2) {
-      kstep(std::integral_constant<int, 0>{}, it);
-      kstep(std::integral_constant<int, 1>{}, it + 1);
+    for (int kt = 0; kt < KT; kt += 2) {
+      kstep(std::integral_constant<int, 0>{});
+      advance_cursor();
+      rd_stage = (rd_stage + 1 == kPipeStages) ? 0 : rd_stage + 1;
+      kstep(std::integral_constant<int, 1>{});
+      advance_cursor();
+      rd_stage = (rd_stage + 1 == kPipeStages) ? 0 : rd_stage + 1;
     }
     // ---- epilogue (same arithmetic and store pattern as gemm_persistent)
     int tm, tn;

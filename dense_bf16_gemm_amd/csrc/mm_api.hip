@@ -55,6 +55,10 @@ struct KernelEntry {
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
+    MM_KP(256, 256, 2, 4, false),
+    MM_KP(256, 256, 4, 2, false),
+    MM_KP(256, 256, 2, 4, true),
+    MM_KP(256, 256, 4, 2, true),
     MM_KP(256, 256, 2, 2, false),
     MM_KP(128, 128, 2, 2, false),
     MM_KP(256, 256, 2, 2, true),
