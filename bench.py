@@ -27,13 +27,14 @@ sys.path.insert(0, ROOT)
 # MI355X bf16 dense MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz (published as 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["dense_bf16_gemm_amd/csrc/gemm_kernel.hpp", "dense_bf16_gemm_amd/csrc/mm_api.hip"]
+CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for name in sorted(n for n in os.listdir(CSRC) if n.endswith(".hpp")):  # the kernel templates
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -93,6 +94,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--config", default=None, help="tile configuration override (mm_set_config)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run three device-to-device copies of BYTES bytes (the reference "
+                         "kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -109,6 +113,14 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copied {src.numel() * 4} bytes three times", file=sys.stderr)
+        return 0
     binding.load()
     if args.config:
         binding.set_config(args.config)
@@ -153,6 +165,9 @@ def main() -> int:
     achieved = w.flops / (mean_launch * 1e-3) / 1e12
 
     traffic = traffic_from_profile(name)
+    tiles = binding.describe_config(w.form, w.M, w.N, w.K, w.layout)
+    cfg = dict(kv.split("=") for kv in tiles.split(","))
+    kernel = f"mmk::{cfg['KERNEL']}<{cfg['BM']},{cfg['BN']},{cfg['WM']},{cfg['WN']},{w.form == 'ffn'}>"
     result = {
         "metric": "TFLOP/s and % of bf16 MFMA peak, 8192^3 linear+bias+GELU, 1 GPU"
         if name == synth.HEADLINE else f"TFLOP/s, {name}, 1 GPU",
@@ -174,7 +189,7 @@ def main() -> int:
             "layout": w.layout,
             "epilogue": w.epilogue,
             "out_dtype": w.out_dtype,
-            "tiles": binding.describe_config(w.form, w.M, w.N, w.K, w.layout),
+            "tiles": tiles,
             "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
         "roofline": {
@@ -184,7 +199,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "mmk::gemm_persistent",
+            "kernel": kernel,
             "launch_ms_mean": round(mean_launch, 5),
             "launch_ms_median": round(statistics.median(per_launch), 5),
             "launch_ms_min": round(min(per_launch), 5),

@@ -431,8 +431,18 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
       layout < MM_NN || layout > MM_TT)
     return fail(MM_ERR_INVALID_VALUE, "bad arguments");
   const Config c = choose_config(form == 1, M, N, K);
-  std::snprintf(buf, (size_t)buflen, "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d",
-                c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe);
+  // the kernel a call of this shape would launch (no HIP call is made)
+  const char* kernel = "none";
+  if (M > 0 && N > 0 && K > 0) {
+    Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
+              false, form == 1};
+    Plan pl;
+    if (plan_host(r, c, &pl) == MM_OK) kernel = pl.kernel->pipe ? "gemm_nt_pipe" : "gemm_persistent";
+    g_last_error.clear();
+  }
+  std::snprintf(buf, (size_t)buflen,
+                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,KERNEL=%s", c.bm, c.bn,
+                c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe, kernel);
   return MM_OK;
 }
 
