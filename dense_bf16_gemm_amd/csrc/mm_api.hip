@@ -21,6 +21,8 @@
 #include "../../include/mm.h"
 #include "gemm_kernel.hpp"
 #include "gemm_nt_pipe.hpp"
+#include "gemm_pingpong.hpp"
+#include "gemm_nt_slab.hpp"
 
 namespace {
 
@@ -37,7 +39,8 @@ mm_status fail(mm_status s, const std::string& msg) {
 struct KernelEntry {
   int bm, bn, wgm, wgn;
   bool a_kc, b_kc, ffn;
-  int pipe;  // 1: the 4-stage K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
+  int pipe;  // 3: whole-line slab ring (gemm_nt_slab), 2: ping-pong (gemm_pingpong),
+             // 1: K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
   const void* fn;
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
 };
@@ -50,11 +53,23 @@ struct KernelEntry {
   {BM, BN, WGM, WGN, true, true, FFN, 1,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_pipe<BM, BN, WGM, WGN, FFN>), {0}}
 
+#define MM_KPP(FFN)                                                                        \
+  {256, 256, 2, 4, true, true, FFN, 2,                                                     \
+   reinterpret_cast<const void*>(&mmk::gemm_pingpong<FFN>), {0}}
+
+#define MM_KS(FFN)                                                                         \
+  {256, 256, 2, 2, true, true, FFN, 3,                                                     \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, FFN>), {0}}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
+    MM_KS(false),
+    MM_KS(true),
+    MM_KPP(false),
+    MM_KPP(true),
     MM_KP(256, 256, 2, 4, false),
     MM_KP(256, 256, 4, 2, false),
     MM_KP(256, 256, 2, 4, true),
@@ -90,7 +105,7 @@ struct Config {
   int xcd = 1;    // XCD-aware remap
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
-  int pipe = 1;   // prefer the 4-stage K-contiguous pipeline where it exists
+  int pipe = 1;   // preferred kernel family: 3 slab ring, 2 ping-pong, 1 pipeline, 0 basic
 };
 
 std::mutex g_cfg_mu;
@@ -125,7 +140,7 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "PIPE") c.pipe = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 1) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 3) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -297,11 +312,14 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
   if (r.ffn && !b_kc) return fail(MM_ERR_UNSUPPORTED, "FFN weights must be [N][K]");
   KernelEntry* k = nullptr;
-  // the pipelined kernel addresses a tile's rows with 32-bit buffer offsets
+  // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
-  if (c.pipe && span < (int64_t(1) << 31))
-    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, 1);
-  if (!k) k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, 0);
+  for (int fam = c.pipe; fam >= 0 && !k; --fam) {
+    if (fam > 0 && span >= (int64_t(1) << 31)) continue;
+    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam);
+  }
+  // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile
+  if (!k) k = find_kernel(c.bm, c.bn, 2, 2, a_kc, b_kc, r.ffn, 0);
   if (!k) return fail(MM_ERR_UNSUPPORTED, "no kernel for this tile configuration, layout and form");
   const int out_bn = r.ffn ? c.bn / 2 : c.bn;
   mmk::GemmParams& p = pl->p;
@@ -325,12 +343,15 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   p.num_tiles = (int)(tm * tn);
   // the pipelined kernel runs k-steps of 32 in pairs: an even count, padded
   // with k-steps past K that read zeros
-  p.k_tiles = k->pipe ? (int)(2 * cdiv(r.K, 2 * mmk::kPipeBK)) : (int)cdiv(r.K, mmk::kBK);
+  p.k_tiles = k->pipe == 3 ? (int)cdiv(r.K, mmk::kSlabK)
+             : k->pipe == 2 ? (int)cdiv(r.K, mmk::kPipeBK)
+             : k->pipe == 1 ? (int)(2 * cdiv(r.K, 2 * mmk::kPipeBK))
+                            : (int)cdiv(r.K, mmk::kBK);
   p.group_m = c.group;
   p.xcd_remap = c.xcd;
   p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
   pl->kernel = k;
-  pl->threads = c.wgm * c.wgn * 64;
+  pl->threads = k->wgm * k->wgn * 64;  // the selected kernel's block size
   pl->grid = 0;
   return MM_OK;
 }
@@ -437,7 +458,11 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
               false, form == 1};
     Plan pl;
-    if (plan_host(r, c, &pl) == MM_OK) kernel = pl.kernel->pipe ? "gemm_nt_pipe" : "gemm_persistent";
+    if (plan_host(r, c, &pl) == MM_OK)
+      kernel = pl.kernel->pipe == 3   ? "gemm_nt_slab"
+               : pl.kernel->pipe == 2 ? "gemm_pingpong"
+               : pl.kernel->pipe      ? "gemm_nt_pipe"
+                                      : "gemm_persistent";
     g_last_error.clear();
   }
   std::snprintf(buf, (size_t)buflen,
