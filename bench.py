@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the bf16 GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
 
 A step is one call of the fused operation on one batch of synthetic input
 already resident in device memory (default: linear + bias + GELU(tanh) at
 M = N = K = 8192, W stored [N][K]).  Prints ONE JSON line with the throughput
-in TFLOP/s (2*M*N*K flops per GEMM), a roofline object for the GEMM kernel
+in TFLOP/s (2*M*N*K flops per GEMM) once the clocks have settled (the
+first launches after idle run at boost clocks, then the board's power limit
+takes over within about 100 launches), a roofline object for the GEMM kernel
 (achieved TFLOP/s from HIP events around every launch on the launch stream,
 against the bf16 dense MFMA peak) and the CPU oracle's throughput on a
 bounded sample of the same workload, timed on this host's cores.
@@ -88,8 +90,8 @@ def cpu_baseline(w, tensors, target_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

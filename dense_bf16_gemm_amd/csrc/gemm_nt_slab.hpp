@@ -1,22 +1,29 @@
 // gemm_nt_slab.hpp -- K-contiguous ("NT") GEMM whose global->LDS copies move
-// whole 128-byte lines.
+// whole 128-byte lines, for 256 x 256 tiles on four waves.
 //
-// Same schedule, MFMA loop and epilogue as gemm_nt_pipe, with the LDS ring
-// reorganised so that each copy instruction reads 8 rows x 128 bytes (64 k)
-// instead of 16 rows x 64 bytes: a line then travels from L2 once instead of
-// twice, which halves the requests the vector L1 has to keep in flight (its
-// pending-request stalls were the main cost of the copies).
-//   * The ring is 5 units of 32 KiB.  A unit holds one operand's 256 rows of
-//     one 64-k "super-step" (rows of 128 bytes, XOR-swizzled as lds_swz);
-//     the A and the weight slab of super-step S take consecutive units.
-//   * The MFMA loop still runs k-steps of 32 (two per super-step), with the
-//     operand fragments read one k-step ahead into a second register set.
-//   * The slabs of super-step S are last read during k-step 2S (which reads
-//     the fragments of k-step 2S+1), so after the barrier at the top of
-//     k-step 2S+1 both units are free.  The copies of super-step S+2 go out
-//     as: A slab during k-step 2S, weight slab during k-step 2S+1.  Each
-//     slab has 2 to 3 k-steps to land; one barrier per super-step publishes
-//     the next super-step's slabs and frees the previous one's.
+// Same persistent schedule, tile order and result as gemm_nt_pipe, with
+// three changes aimed at keeping one wave per SIMD issuing MFMAs:
+//   * Copies.  Each copy instruction reads 8 rows x 128 bytes (64 k) instead
+//     of 16 rows x 64 bytes, so every cache line travels from L2 once and the
+//     vector L1 keeps half as many requests in flight.  The LDS ring is 5
+//     units of 32 KiB; a unit holds one operand's 256 rows of one 64-k
+//     "super-step" (XOR-swizzled rows of 128 bytes), and the A and weight
+//     slabs of a super-step sit in consecutive units.  The slabs of
+//     super-step q+2 are copied during super-step q (A during its first
+//     k-step, the weight slab during its second), and one wait + barrier per
+//     super-step publishes q+1 and frees q (the write-after-read hazard of
+//     issue "Automate performant Hopper matmul", section "Syncing issues";
+//     prefetch distance > 1 as its section "K loop efficiency" asks).
+//   * Registers.  The MFMAs of a k-step run row by row (8 output-row blocks
+//     of 16 x 128); the activation fragment of row r is dead after row r and
+//     is refilled at once with the next k-step's fragment, while the weight
+//     fragments are double-buffered.  24 live fragments instead of 32 leave
+//     the accumulators in place (no AGPR shuffles, no spills).
+//   * The K loop of a tile has no tile bookkeeping: the load cursor moves to
+//     the next tile once, before the last two super-steps, whose copies fetch
+//     that tile's first slabs (so they land while this tile's epilogue runs:
+//     section "Syncing persistent matmuls").
+// The host uses this kernel only when K spans at least two super-steps.
 #pragma once
 
 #include "gemm_nt_pipe.hpp"
@@ -26,6 +33,21 @@ namespace mmk {
 constexpr int kSlabK = 64;       // k per super-step
 constexpr int kSlabRowB = 128;   // LDS bytes per row of a unit
 constexpr int kSlabUnits = 5;
+
+// GELU(tanh) as t / (1 + 2^(t (c1 + c2 t^2))) with c1 = -2 sqrt(2/pi) log2(e)
+// and c2 = 0.044715 c1: the same function as 0.5 t (1 + tanh z), rewritten
+// so that one exp2 and one reciprocal remain.
+__device__ __forceinline__ float gelu_tanh_fast(float t) {
+  constexpr float c1 = -2.3022081983f;   // -2 * 0.7978845608 * 1.4426950409
+  constexpr float c2 = -0.1029432396f;   // c1 * 0.044715
+  const float e = __builtin_amdgcn_exp2f(t * __builtin_fmaf(c2, t * t, c1));
+  return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// SiLU as g / (1 + 2^(-g log2 e)).
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
+}
 
 template <int BM, int BN, int WGM, int WGN, bool FFN>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -37,11 +59,10 @@ gemm_nt_slab(GemmParams p) {
   constexpr int FN = WTN / 16;
   constexpr int OUT_BN = FFN ? BN / 2 : BN;
   constexpr int UNIT = 256 * kSlabRowB;  // 32 KiB
-  static_assert(BM == 256 && BN == 256, "a unit holds 256 rows");
+  static_assert(BM == 256 && BN == 256 && NW == 4, "a unit holds 256 rows; four waves");
+  static_assert(FM == 8 && FN == 8, "row schedule assumes 8 x 8 fragments per wave");
   constexpr int CPS = 256 / 8 / NW;  // 1 KiB copies per wave per slab
-  static_assert(CPS * NW * 8 == 256, "copy split");
-  static_assert(FN % 2 == 0 && (!FFN || FN % 4 == 0), "fragment pairs");
-  static_assert(WTN % 32 == 0 && WTM % 32 == 0, "wave tile");
+  static_assert(CPS == FM, "one copy per MFMA row");
 
   __shared__ __attribute__((aligned(1024))) char smem[kSlabUnits * UNIT];
 
@@ -54,38 +75,47 @@ gemm_nt_slab(GemmParams p) {
   const int wg = remap_workgroup(blockIdx.x, G, p.xcd_remap);
   if (wg >= p.num_tiles) return;
   const int my_tiles = (p.num_tiles - wg + G - 1) / G;
-  const int KS = p.k_tiles;  // super-steps of 64 per tile
+  const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
   const int M = p.M, N = p.N, K = p.K;
   const int64_t ld = K;
 
   // ---- copies: lane L of a 1 KiB copy fills unit row 8j + L/8, physical
   // chunk L%8, from logical chunk (L%8) ^ lds_swz(row).  Bits 0..2 of that
-  // row are L/8 and bit 4 is bit 1 of j; a wave's copies j = i*NW + wave
-  // all share bit 1 of j when NW is a multiple of 4, so the chunk is fixed.
-  static_assert(NW % 4 == 0, "copy chunk constant per wave");
+  // row are L/8 and bit 4 is bit 1 of j = 4c + wave, i.e. bit 1 of the wave,
+  // so the logical chunk of a lane is the same for all its copies.
   const int crow = lane >> 3;
-  const int cchunk = (lane & 7) ^ lds_swz(crow + 8 * (wave & ~1));
+  const int cchunk = (lane & 7) ^ lds_swz(crow + 8 * (wave & 2));
   const uint32_t row_bytes = (uint32_t)ld * 2u;
   const uint32_t lane_base = (uint32_t)crow * row_bytes + 16u * (uint32_t)cchunk;
   constexpr int kRsrcWord3 = 0x00020000;
 
-  uint64_t a_base = 0, b0_base = 0, b1_base = 0;
-  uint32_t a_rec = 0, b_rec = 0;
-  int ld_alt = 0;
-  auto enter_tile = [&](int tile_i) __attribute__((always_inline)) {
+  // Descriptors of the tile the copies currently fetch (cur) and of the
+  // workgroup's next tile (nxt; the current one again after the last tile,
+  // whose re-fetched slabs are never read).
+  struct TileDesc {
+    uint64_t a_base, b0_base, b1_base;
+    uint32_t a_rec, b_rec;
+    int alt;
+  };
+  auto tile_desc = [&](int tile_i) __attribute__((always_inline)) {
     int tm, tn;
     tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * BM;
     const int mrows = (M - m0) < BM ? (M - m0) : BM;
-    a_base = reinterpret_cast<uint64_t>(p.A + (int64_t)m0 * ld);
-    a_rec = (uint32_t)mrows * row_bytes;
     const int n0 = tn * OUT_BN;
     const int nrows = (N - n0) < OUT_BN ? (N - n0) : OUT_BN;
-    b_rec = (uint32_t)nrows * row_bytes;
-    b0_base = reinterpret_cast<uint64_t>(p.B + (int64_t)n0 * ld);
-    b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + (int64_t)n0 * ld) : b0_base;
-    ld_alt = p.k_alt && (tile_i & 1);
+    TileDesc d;
+    d.a_base = reinterpret_cast<uint64_t>(p.A + (int64_t)m0 * ld);
+    d.a_rec = (uint32_t)mrows * row_bytes;
+    d.b_rec = (uint32_t)nrows * row_bytes;
+    d.b0_base = reinterpret_cast<uint64_t>(p.B + (int64_t)n0 * ld);
+    d.b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + (int64_t)n0 * ld) : d.b0_base;
+    d.alt = p.k_alt && (tile_i & 1);
+    return d;
   };
+  TileDesc cur = tile_desc(0);
+  // Buffer descriptors are rebuilt from wave-uniform values at each use so
+  // that they stay in scalar registers.
   auto rsrc = [&](uint64_t base, uint32_t rec) __attribute__((always_inline)) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
@@ -93,18 +123,21 @@ gemm_nt_slab(GemmParams p) {
     return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, (int)__builtin_amdgcn_readfirstlane(rec),
                                              kRsrcWord3);
   };
+  // Byte offset of this lane's chunk of super-step ks of the fetched tile;
+  // chunks past K get bit 31 set, which the buffer range check turns into zeros.
   auto koff_of = [&](int ks) __attribute__((always_inline)) {
-    const int k0 = (ld_alt ? (KS - 1 - ks) : ks) * kSlabK;
+    const int k0 = (cur.alt ? (KS - 1 - ks) : ks) * kSlabK;
     return lane_base + 2u * (uint32_t)k0 + ((k0 + 8 * cchunk) < K ? 0u : 0x80000000u);
   };
-  // copy c (0..CPS-1) of this wave for the A slab / the weight slab
+  // Copy c of this wave for the A slab / the weight slab into unit `unit`.
+  // (The descriptor type is spelled out: deducing it leaves the host stub of
+  // the kernel uninstantiated.)
   auto copy_a = [&](int c, uint32_t koff, int unit) __attribute__((always_inline)) {
     const int j = c * NW + wave;
-    // (typed explicitly: deducing the builtin's type leaves the host stub uninstantiated)
-    const __amdgpu_buffer_rsrc_t r = rsrc(a_base, a_rec);
+    const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base, cur.a_rec);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024),
-        16, koff + (uint32_t)(8 * j) * row_bytes, 0, 0, 0);
+        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024), 16,
+        koff + (uint32_t)(8 * j) * row_bytes, 0, 0, 0);
   };
   auto copy_b = [&](int c, uint32_t koff, int unit) __attribute__((always_inline)) {
     const int j = c * NW + wave;
@@ -117,170 +150,188 @@ gemm_nt_slab(GemmParams p) {
       up = within >= WTN / 2;
       prow = wb * (WTN / 2) + (up ? within - WTN / 2 : within);
     }
-    const __amdgpu_buffer_rsrc_t r = rsrc(up ? b1_base : b0_base, b_rec);
+    const __amdgpu_buffer_rsrc_t r = rsrc(up ? cur.b1_base : cur.b0_base, cur.b_rec);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r,
-        (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024), 16,
+        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024), 16,
         koff + (uint32_t)prow * row_bytes, 0, 0, 0);
   };
-
-  // ---- load cursor: super-step (ld_tile, ld_ks) whose slabs are copied next
-  int ld_tile = 0, ld_ks = 0, ld_unit = 0;  // ld_unit: unit of its A slab
-  enter_tile(0);
-  auto advance_cursor = [&]() __attribute__((always_inline)) {
-    ld_unit = (ld_unit + 2) % kSlabUnits;
-    if (ld_tile < my_tiles) {
-      if (++ld_ks == KS) {
-        ld_ks = 0;
-        ++ld_tile;
-        if (ld_tile < my_tiles) enter_tile(ld_tile);
-        else ld_ks = KS - 1;  // past the end: re-copy the last super-step (never read)
-      }
-    }
+  auto next_unit = [](int u) __attribute__((always_inline)) {
+    return u + 1 == kSlabUnits ? 0 : u + 1;
   };
-  auto next_unit = [](int u) { return u + 1 == kSlabUnits ? 0 : u + 1; };
 
-  // ---- fragments: 128-byte rows, k-step half h uses chunks 4h..4h+3
+  // ---- fragments: 128-byte rows; k-step half h uses logical chunks 4h..4h+3.
+  // For A rows wrow_a + 16 fm + lx the swizzle is (lx & 7) ^ 4 (fm & 1); for
+  // the comb rows of the weight fragments wrow_b + 32 (fn >> 1) + 8 (lx >> 2)
+  // + 4 (fn & 1) + (lx & 3) it is (lx & 3) ^ 4 ((fn & 1) ^ bit 3 of lx).
+  // Either way the chunk is a lane constant XOR 4 (h ^ (f & 1)), which flips
+  // bit 6 of the byte offset.
   const int lx = lane & 15;
   const int lk = lane >> 4;
   const int wrow_a = wave_m * WTM;
   const int wrow_b = wave_n * WTN;
-  // Swizzled chunk of k-step half h: (4h + lk) ^ lds_swz(row).  For A rows
-  // wrow_a + 16q + lx, lds_swz = (lx & 7) ^ 4q; for the comb rows of the
-  // weight fragments wrow_b + 8(lx>>2) + 4q + (lx&3), lds_swz = (lx & 3) ^
-  // 4(q ^ bit 3 of lx).  Either way the chunk is a lane constant XOR 4(h^q),
-  // so two offsets per operand cover every (h, q).
   const uint32_t a_x0 = (uint32_t)((wrow_a + lx) * kSlabRowB + ((lk ^ (lx & 7)) << 4));
   const uint32_t b_x0 = (uint32_t)((wrow_b + 8 * (lx >> 2) + (lx & 3)) * kSlabRowB +
                                    ((lk ^ (lx & 3) ^ (((lx >> 3) & 1) << 2)) << 4));
 
-  bf16x8 fa[2][FM], fb[2][FN];
+  bf16x8 fa[FM];     // activation fragments, refilled row by row
+  bf16x8 fb[2][FN];  // weight fragments, double-buffered
   f32x4 acc[FM][FN];
 
-  // fragments of k-step half h from the slabs in units ua (A) and ub (weight)
-  auto read_frag = [&](int f, int h, int ua, int ub, bf16x8* a, bf16x8* b)
-      __attribute__((always_inline)) {
-    if (f < FN) {
-      const char* base = smem + ub * UNIT;
-      const int q = f & 1;
-      const uint32_t off = ((h ^ q) ? (b_x0 ^ 64u) : b_x0) + (uint32_t)((4 * q + 32 * (f >> 1)) * kSlabRowB);
-      b[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
-    } else {
-      const int fm = f - FN;
-      const char* base = smem + ua * UNIT;
-      const int q = fm & 1;
-      const uint32_t off = ((h ^ q) ? (a_x0 ^ 64u) : a_x0) + (uint32_t)(16 * fm * kSlabRowB);
-      a[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
+  auto read_a = [&](int fm, int h, uint32_t ubase) __attribute__((always_inline)) {
+    const uint32_t off = (((h ^ fm) & 1) ? (ubase ^ 64u) : ubase) + (uint32_t)(16 * fm * kSlabRowB);
+    fa[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + off));
+  };
+  auto read_b = [&](int set, int fn, int h, uint32_t ubase) __attribute__((always_inline)) {
+    const uint32_t off = (((h ^ fn) & 1) ? (ubase ^ 64u) : ubase) +
+                         (uint32_t)((4 * (fn & 1) + 32 * (fn >> 1)) * kSlabRowB);
+    fb[set][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + off));
+  };
+  // half of the MFMAs of output-row block r with weight set `set`
+  auto mfma_half = [&](int r, int set, int half) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FN / 2; ++i) {
+      const int fn = half * (FN / 2) + i;
+      acc[r][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[set][fn], fa[r], acc[r][fn], 0, 0, 0);
     }
   };
 
-  // ---- prologue: slabs of super-steps 0 and 1 in flight; fragments of
-  // k-step 0 in register set 0.  (Each wave: CPS copies per slab.)
+  // ---- ring: super-step q (counted over all tiles of this workgroup) has
+  // its A slab in unit (2q) % 5 and its weight slab in unit (2q + 1) % 5.
+  int cur_unit = 0;  // A unit of the current super-step
   {
+    // prologue: slabs of super-steps 0 and 1 of the first tile (KS >= 2)
+#pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t koff = koff_of(ld_ks);
-      const int ua = ld_unit, ub = next_unit(ld_unit);
+      const uint32_t koff = koff_of(s);
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) copy_a(c, koff, ua);
+      for (int c = 0; c < CPS; ++c) copy_a(c, koff, 2 * s);
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) copy_b(c, koff, ub);
-      advance_cursor();
+      for (int c = 0; c < CPS; ++c) copy_b(c, koff, 2 * s + 1);
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * CPS));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < FM; ++f) read_a(f, 0, a_x0);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) read_b(0, f, 0, b_x0 + (uint32_t)UNIT);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * CPS));
-  __builtin_amdgcn_s_barrier();
-  int cur_unit = 0;  // unit of the A slab of the current super-step
-#pragma unroll
-  for (int f = 0; f < FM + FN; ++f) read_frag(f, 0, 0, 1, fa[0], fb[0]);
 
-  constexpr int NMFMA = FM * FN;
-  constexpr int NDS = FM + FN;
-  // One k-step: MFMAs on register set P, fragments of the next k-step
-  // (half nh of the slabs in units nua/nub) into set P^1, and the CPS copies
-  // of one slab (A if copy_is_a) interleaved CPS-way.
-  auto kstep = [&](auto par, int nh, int nua, int nub, bool copy_is_a, uint32_t koff, int cunit)
-      __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;
+  // One super-step q: k-steps 2q (half 0, weight set 0) and 2q+1 (half 1,
+  // weight set 1).  Fragments of the next k-step are read as soon as their
+  // registers are free; the copies of super-step q+2 (lane offset koff in
+  // the fetched tile) go out one per MFMA row.
+  auto super_step = [&](uint32_t koff) __attribute__((always_inline)) {
+    const int ua = cur_unit, ub = next_unit(ua);
+    const int nua = next_unit(ub), nub = next_unit(nua);  // super-step q+1
+    const int cua = next_unit(nub);                        // A slab of q+2
+    const int cub = ua;                                    // weight slab of q+2
+    const uint32_t a_cur = a_x0 + (uint32_t)(ua * UNIT), b_cur = b_x0 + (uint32_t)(ub * UNIT);
+    const uint32_t a_nxt = a_x0 + (uint32_t)(nua * UNIT), b_nxt = b_x0 + (uint32_t)(nub * UNIT);
+
+    // k-step 2q: MFMAs on half 0; half 1 of q (same units) into fa and fb[1]
 #pragma unroll
-    for (int c = 0; c < CPS; ++c) {
-      if (copy_is_a) copy_a(c, koff, cunit);
-      else copy_b(c, koff, cunit);
-#pragma unroll
-      for (int f = (c * NDS) / CPS; f < ((c + 1) * NDS) / CPS; ++f)
-        read_frag(f, nh, nua, nub, fa[P ^ 1], fb[P ^ 1]);
-#pragma unroll
-      for (int i = (c * NMFMA) / CPS; i < ((c + 1) * NMFMA) / CPS; ++i) {
-        const int fm = i / FN, fn = i % FN;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[P][fn], fa[P][fm], acc[fm][fn], 0, 0, 0);
+    for (int r = 0; r < FM; ++r) {
+      mfma_half(r, 0, 0);
+      copy_a(r, koff, cua);
+      if (r < FN / 2) {
+        read_b(1, 2 * r, 1, b_cur);
+        read_b(1, 2 * r + 1, 1, b_cur);
       }
       __builtin_amdgcn_sched_barrier(0);
+      mfma_half(r, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(r, 1, a_cur);
+      __builtin_amdgcn_sched_barrier(0);
     }
+
+    // k-step 2q+1, row 0: its fragments are already in registers
+    mfma_half(0, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half(0, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // This wave's copies of q+1 have landed (only the A slab of q+2 may still
+    // be in flight) and its reads of q's units are done; after the barrier
+    // q+1 is visible to all waves and q's units may be overwritten.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(0, 0, a_nxt);
+    // rows 1..7: half 0 of q+1 into fa and fb[0]; the weight slab of q+2
+#pragma unroll
+    for (int r = 1; r < FM; ++r) {
+      mfma_half(r, 1, 0);
+      if (r == 1) copy_b(0, koff, cub);
+      copy_b(r, koff, cub);
+      if (r <= FN / 2) {
+        read_b(0, 2 * (r - 1), 0, b_nxt);
+        read_b(0, 2 * (r - 1) + 1, 0, b_nxt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(r, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(r, 0, a_nxt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur_unit = nua;
   };
 
-  for (int tile_i = 0; tile_i < my_tiles; ++tile_i) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < KS; ++ks) {
-      // super-step S = this one; its slabs are in units cur_unit, cur_unit+1
-      const int ua = cur_unit, ub = next_unit(cur_unit);
-      const int nua = next_unit(ub), nub = next_unit(nua);  // super-step S+1
-      const uint32_t koff = koff_of(ld_ks);                  // super-step S+2
-      const int cua = ld_unit, cub = next_unit(ld_unit);
-      // k-step 2S: fragments of 2S+1 (same slabs, half 1); copy A slab of S+2
-      kstep(std::integral_constant<int, 0>{}, 1, ua, ub, true, koff, cua);
-      // top of k-step 2S+1: own copies of S+1 landed (the A slab of S+2 may
-      // still fly); then publish S+1 and free the units of S
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step 2S+1: fragments of 2S+2 (S+1, half 0); copy weight slab of S+2
-      kstep(std::integral_constant<int, 1>{}, 0, nua, nub, false, koff, cub);
-      advance_cursor();
-      cur_unit = nua;
-    }
-
-    // ---- epilogue (as gemm_nt_pipe)
-    int tm, tn;
-    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-    const int m_base = tm * BM + wrow_a + lx;
-    const int g8 = 8 * lk;
-    constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
-    const bool has_bias = (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU);
-    const bool gelu = (p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU);
+  // ---- epilogue straight from the accumulators.  A lane holds 8
+  // consecutive columns of a fragment pair; the two pairs that make up one
+  // 128-byte output line are stored back to back.  F32 / ACT / CHECKED are
+  // compile-time in the fast paths (interior tiles with aligned rows) and
+  // run-time in the one checked path for edge tiles.
+  const bool has_bias = (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU);
+  const bool act_on = FFN ? (p.epi == EPI_SWIGLU) : (p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU);
+  const bool bias_vec = (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
+  constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
+  auto epilogue = [&](int m0, int n0, auto f32, auto act, auto checked) __attribute__((always_inline)) {
+    const int m_base = m0 + wrow_a + lx;
+    int ncol[PAIRS];
+    float bv[PAIRS][8];
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
-      const int n = FFN ? tn * OUT_BN + wave_n * (WTN / 2) + 32 * pr + g8
-                        : tn * OUT_BN + wrow_b + 32 * pr + g8;
-      float bv[8];
+      const int n = FFN ? n0 + wave_n * (WTN / 2) + 32 * pr + 8 * lk : n0 + wrow_b + 32 * pr + 8 * lk;
+      ncol[pr] = n;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float b = 0.f;
-        if (has_bias && n + j < N) b = __builtin_bit_cast(float, (uint32_t)p.bias[n + j] << 16);
-        bv[j] = b;
+      for (int j = 0; j < 8; ++j) bv[pr][j] = 0.f;
+      if constexpr (!FFN) {
+        if (has_bias && bias_vec && n + 8 <= N) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(p.bias + n);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bv[pr][2 * j] = __builtin_bit_cast(float, w[j] << 16);
+            bv[pr][2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+          }
+        } else if (has_bias) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (n + j < N) bv[pr][j] = __builtin_bit_cast(float, (uint32_t)p.bias[n + j] << 16);
+        }
       }
+    }
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int m = m_base + 16 * fm;
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = m_base + 16 * fm;
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        const int n = ncol[pr];
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float a = acc[fm][2 * pr + (j >> 2)][j & 3];
-          float y;
           if constexpr (FFN) {
             const float u = acc[fm][FN / 2 + 2 * pr + (j >> 2)][j & 3];
-            y = (p.epi == EPI_SWIGLU) ? silu(a) * u : a * u;
+            v[j] = (act ? silu_fast(a) : a) * u;
           } else {
-            const float t = a + bv[j];
-            y = gelu ? gelu_tanh(t) : t;
+            const float t = a + bv[pr][j];
+            v[j] = act ? gelu_tanh_fast(t) : t;
           }
-          v[j] = y;
         }
-        if (m >= M) continue;
-        if (p.out_f32) {
+        if (checked && m >= M) continue;
+        const bool vec = !checked || (p.out_vec && n + 8 <= N);
+        if (f32) {
           float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * N + n;
-          if (p.out_vec && n + 8 <= N) {
+          if (vec) {
             reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
             reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
           } else {
@@ -290,7 +341,7 @@ gemm_nt_slab(GemmParams p) {
           }
         } else {
           uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m * N + n;
-          if (p.out_vec && n + 8 <= N) {
+          if (vec) {
             u32x4 w;
             w[0] = pack_bf16x2(v[0], v[1]);
             w[1] = pack_bf16x2(v[2], v[3]);
@@ -304,6 +355,41 @@ gemm_nt_slab(GemmParams p) {
           }
         }
       }
+    }
+  };
+
+  for (int tile_i = 0; tile_i < my_tiles; ++tile_i) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The copies of super-step ks fetch this tile's super-step ks + 2, and
+    // from ks = KS - 2 on the next tile's super-steps 0 and 1.
+    const TileDesc nxt = tile_desc(tile_i + 1 < my_tiles ? tile_i + 1 : tile_i);
+    for (int ks = 0; ks < KS; ++ks) {
+      int lks = ks + 2;
+      if (lks >= KS) {
+        lks -= KS;
+        cur = nxt;
+      }
+      super_step(koff_of(lks));
+    }
+
+    int tm, tn;
+    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * OUT_BN;
+    using T = std::true_type;
+    using F = std::false_type;
+    if (p.out_vec && m0 + BM <= M && n0 + OUT_BN <= N) {
+      if (FFN || !p.out_f32) {
+        if (act_on) epilogue(m0, n0, F{}, T{}, F{});
+        else epilogue(m0, n0, F{}, F{}, F{});
+      } else {
+        if (act_on) epilogue(m0, n0, T{}, T{}, F{});
+        else epilogue(m0, n0, T{}, F{}, F{});
+      }
+    } else {
+      epilogue(m0, n0, p.out_f32 != 0, act_on, T{});
     }
   }
 }

@@ -105,7 +105,7 @@ struct Config {
   int xcd = 1;    // XCD-aware remap
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
-  int pipe = 1;   // preferred kernel family: 3 slab ring, 2 ping-pong, 1 pipeline, 0 basic
+  int pipe = 3;   // preferred kernel family: 3 slab ring, 2 ping-pong, 1 pipeline, 0 basic
 };
 
 std::mutex g_cfg_mu;
@@ -316,6 +316,8 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
+    // the slab kernel keeps two super-steps of 64 k in flight: K > 64
+    if (fam == 3 && r.K <= mmk::kSlabK) continue;
     k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile

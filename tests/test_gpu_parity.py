@@ -27,14 +27,14 @@ pytestmark = pytest.mark.gpu
 CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
     "BM=256,BN=256,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=2",
-    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2",
+    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=1",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
 ]
 FFN_CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
     "BM=256,BN=256,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=2",
-    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2",
+    "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=1",
     "BM=128,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=128,BN=128,WM=2,WN=2,G=2,XCD=0,KALT=0",
 ]
