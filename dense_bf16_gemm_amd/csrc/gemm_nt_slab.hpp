@@ -23,7 +23,8 @@
 //     the next tile once, before the last two super-steps, whose copies fetch
 //     that tile's first slabs (so they land while this tile's epilogue runs:
 //     section "Syncing persistent matmuls").
-// The host uses this kernel only when K spans at least two super-steps.
+// The host uses this kernel only when K is a multiple of the 64-k super-step
+// and spans at least two of them (ragged K runs gemm_nt_pipe).
 #pragma once
 
 #include "gemm_nt_pipe.hpp"
@@ -72,9 +73,12 @@ gemm_nt_slab(GemmParams p) {
   const int wave_m = wave / WGN;
   const int wave_n = wave % WGN;
   const int G = gridDim.x;
-  const int wg = remap_workgroup(blockIdx.x, G, p.xcd_remap);
+  // (integer division runs on the vector unit; readfirstlane hands the
+  // wave-uniform results back to scalar registers, so that all descriptor
+  // and offset arithmetic below stays scalar)
+  const int wg = __builtin_amdgcn_readfirstlane(remap_workgroup(blockIdx.x, G, p.xcd_remap));
   if (wg >= p.num_tiles) return;
-  const int my_tiles = (p.num_tiles - wg + G - 1) / G;
+  const int my_tiles = __builtin_amdgcn_readfirstlane((p.num_tiles - wg + G - 1) / G);
   const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
   const int M = p.M, N = p.N, K = p.K;
   const int64_t ld = K;
@@ -100,6 +104,8 @@ gemm_nt_slab(GemmParams p) {
   auto tile_desc = [&](int tile_i) __attribute__((always_inline)) {
     int tm, tn;
     tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
     const int m0 = tm * BM;
     const int mrows = (M - m0) < BM ? (M - m0) : BM;
     const int n0 = tn * OUT_BN;
@@ -123,37 +129,48 @@ gemm_nt_slab(GemmParams p) {
     return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, (int)__builtin_amdgcn_readfirstlane(rec),
                                              kRsrcWord3);
   };
-  // Byte offset of this lane's chunk of super-step ks of the fetched tile;
-  // chunks past K get bit 31 set, which the buffer range check turns into zeros.
-  auto koff_of = [&](int ks) __attribute__((always_inline)) {
-    const int k0 = (cur.alt ? (KS - 1 - ks) : ks) * kSlabK;
-    return lane_base + 2u * (uint32_t)k0 + ((k0 + 8 * cchunk) < K ? 0u : 0x80000000u);
-  };
-  // Copy c of this wave for the A slab / the weight slab into unit `unit`.
-  // (The descriptor type is spelled out: deducing it leaves the host stub of
-  // the kernel uninstantiated.)
-  auto copy_a = [&](int c, uint32_t koff, int unit) __attribute__((always_inline)) {
-    const int j = c * NW + wave;
-    const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base, cur.a_rec);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024), 16,
-        koff + (uint32_t)(8 * j) * row_bytes, 0, 0, 0);
-  };
-  auto copy_b = [&](int c, uint32_t koff, int unit) __attribute__((always_inline)) {
-    const int j = c * NW + wave;
-    const int r0 = 8 * j;
-    int prow = r0;
-    bool up = false;
+  // Copy c of this wave fills unit rows 8j .. 8j+7, j = 4c + wave.  Each
+  // lane's vector offset is a constant (voff_*: its row and chunk); the k
+  // position of the super-step moves the descriptor's base instead, with the
+  // record count shrunk by the same amount, so rows past the tile's last row
+  // still fail the range check and read as zeros.  No vector instruction is
+  // spent on addressing in the K loop.
+  // weight row of copy c's first row, and whether it is an up-weight row
+  auto wrow_of = [&](int c, bool* up) __attribute__((always_inline)) -> int {
+    const int r0 = 8 * (c * NW + wave);
+    *up = false;
     if constexpr (FFN) {
       // each wave column's WTN weight rows: WTN/2 gate rows, then the up rows
       const int wb = r0 / WTN, within = r0 % WTN;
-      up = within >= WTN / 2;
-      prow = wb * (WTN / 2) + (up ? within - WTN / 2 : within);
+      *up = within >= WTN / 2;
+      return wb * (WTN / 2) + (*up ? within - WTN / 2 : within);
     }
-    const __amdgpu_buffer_rsrc_t r = rsrc(up ? cur.b1_base : cur.b0_base, cur.b_rec);
+    return r0;
+  };
+  // first k of super-step ks of the fetched tile
+  auto k0_of = [&](int ks) __attribute__((always_inline)) {
+    const int alt = __builtin_amdgcn_readfirstlane(cur.alt);
+    return (alt ? (KS - 1 - ks) : ks) * kSlabK;
+  };
+  // Copy c of this wave for the A slab / the weight slab of the super-step at
+  // k byte offset kbytes into unit `unit`.
+  // (The lane offsets are loop-invariant and stay in registers.  They are
+  // written out inline: passing them through a helper or an array leaves the
+  // host stub of the kernel uninstantiated, as does deducing the descriptor
+  // type.)
+  auto copy_a = [&](int c, uint32_t kbytes, int unit) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base + kbytes, cur.a_rec - kbytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + j * 1024), 16,
-        koff + (uint32_t)prow * row_bytes, 0, 0, 0);
+        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
+        lane_base + (uint32_t)(8 * (c * NW + wave)) * row_bytes, 0, 0, 0);
+  };
+  auto copy_b = [&](int c, uint32_t kbytes, int unit) __attribute__((always_inline)) {
+    bool up;
+    const int prow = wrow_of(c, &up);
+    const __amdgpu_buffer_rsrc_t r = rsrc((up ? cur.b1_base : cur.b0_base) + kbytes, cur.b_rec - kbytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
+        lane_base + (uint32_t)prow * row_bytes, 0, 0, 0);
   };
   auto next_unit = [](int u) __attribute__((always_inline)) {
     return u + 1 == kSlabUnits ? 0 : u + 1;
@@ -202,11 +219,11 @@ gemm_nt_slab(GemmParams p) {
     // prologue: slabs of super-steps 0 and 1 of the first tile (KS >= 2)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t koff = koff_of(s);
+      const uint32_t kbytes = 2u * (uint32_t)k0_of(s);
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) copy_a(c, koff, 2 * s);
+      for (int c = 0; c < CPS; ++c) copy_a(c, kbytes, 2 * s);
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) copy_b(c, koff, 2 * s + 1);
+      for (int c = 0; c < CPS; ++c) copy_b(c, kbytes, 2 * s + 1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * CPS));
     __builtin_amdgcn_s_barrier();
@@ -215,24 +232,31 @@ gemm_nt_slab(GemmParams p) {
 #pragma unroll
     for (int f = 0; f < FN; ++f) read_b(0, f, 0, b_x0 + (uint32_t)UNIT);
   }
+  // An LDS wait before each tile's K loop (free: the reads are long done by
+  // then) lets the compiler's wait placement inside the loop follow the loop's
+  // own read order instead of merging it with the prologue's or epilogue's.
+  constexpr int kLgkmDrained = waitcnt_vm_lgkm0(63);
 
   // One super-step q: k-steps 2q (half 0, weight set 0) and 2q+1 (half 1,
   // weight set 1).  Fragments of the next k-step are read as soon as their
-  // registers are free; the copies of super-step q+2 (lane offset koff in
-  // the fetched tile) go out one per MFMA row.
-  auto super_step = [&](uint32_t koff) __attribute__((always_inline)) {
+  // registers are free; the copies of super-step q+2 (first k k0_fetch in
+  // the fetched tile) go out one per MFMA row.  k-step 2q+1 runs its rows in the order 4..7, 0..3, so the
+  // fragment read last in a k-step is needed four rows into the next one
+  // and no k-step starts by waiting on LDS.
+  uint32_t a_cur = a_x0, b_cur = b_x0 + (uint32_t)UNIT;  // units of super-step q
+  auto super_step = [&](int k0_fetch) __attribute__((always_inline)) {
+    const uint32_t kbytes = 2u * (uint32_t)k0_fetch;
     const int ua = cur_unit, ub = next_unit(ua);
     const int nua = next_unit(ub), nub = next_unit(nua);  // super-step q+1
     const int cua = next_unit(nub);                        // A slab of q+2
     const int cub = ua;                                    // weight slab of q+2
-    const uint32_t a_cur = a_x0 + (uint32_t)(ua * UNIT), b_cur = b_x0 + (uint32_t)(ub * UNIT);
     const uint32_t a_nxt = a_x0 + (uint32_t)(nua * UNIT), b_nxt = b_x0 + (uint32_t)(nub * UNIT);
 
     // k-step 2q: MFMAs on half 0; half 1 of q (same units) into fa and fb[1]
 #pragma unroll
     for (int r = 0; r < FM; ++r) {
       mfma_half(r, 0, 0);
-      copy_a(r, koff, cua);
+      copy_a(r, kbytes, cua);
       if (r < FN / 2) {
         read_b(1, 2 * r, 1, b_cur);
         read_b(1, 2 * r + 1, 1, b_cur);
@@ -244,10 +268,10 @@ gemm_nt_slab(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // k-step 2q+1, row 0: its fragments are already in registers
-    mfma_half(0, 1, 0);
+    // k-step 2q+1, first row (4): its fragments are already in registers
+    mfma_half(4, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_half(0, 1, 1);
+    mfma_half(4, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     // This wave's copies of q+1 have landed (only the A slab of q+2 may still
     // be in flight) and its reads of q's units are done; after the barrier
@@ -255,16 +279,18 @@ gemm_nt_slab(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_a(0, 0, a_nxt);
-    // rows 1..7: half 0 of q+1 into fa and fb[0]; the weight slab of q+2
+    read_a(4, 0, a_nxt);
+    // rows 5, 6, 7, 0, 1, 2, 3: half 0 of q+1 into fa and fb[0]; the weight
+    // slab of q+2
 #pragma unroll
-    for (int r = 1; r < FM; ++r) {
+    for (int p = 1; p < FM; ++p) {
+      const int r = (p + 4) & 7;
       mfma_half(r, 1, 0);
-      if (r == 1) copy_b(0, koff, cub);
-      copy_b(r, koff, cub);
-      if (r <= FN / 2) {
-        read_b(0, 2 * (r - 1), 0, b_nxt);
-        read_b(0, 2 * (r - 1) + 1, 0, b_nxt);
+      if (p == 1) copy_b(0, kbytes, cub);
+      copy_b(p, kbytes, cub);
+      if (p <= FN / 2) {
+        read_b(0, 2 * (p - 1), 0, b_nxt);
+        read_b(0, 2 * (p - 1) + 1, 0, b_nxt);
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(r, 1, 1);
@@ -273,6 +299,8 @@ gemm_nt_slab(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     cur_unit = nua;
+    a_cur = a_nxt;
+    b_cur = b_nxt;
   };
 
   // ---- epilogue straight from the accumulators.  A lane holds 8
@@ -366,13 +394,14 @@ gemm_nt_slab(GemmParams p) {
     // The copies of super-step ks fetch this tile's super-step ks + 2, and
     // from ks = KS - 2 on the next tile's super-steps 0 and 1.
     const TileDesc nxt = tile_desc(tile_i + 1 < my_tiles ? tile_i + 1 : tile_i);
+    __builtin_amdgcn_s_waitcnt(kLgkmDrained);
     for (int ks = 0; ks < KS; ++ks) {
       int lks = ks + 2;
       if (lks >= KS) {
         lks -= KS;
         cur = nxt;
       }
-      super_step(koff_of(lks));
+      super_step(k0_of(lks));
     }
 
     int tm, tn;

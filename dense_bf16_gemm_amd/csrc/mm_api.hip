@@ -316,8 +316,8 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
-    // the slab kernel keeps two super-steps of 64 k in flight: K > 64
-    if (fam == 3 && r.K <= mmk::kSlabK) continue;
+    // the slab kernel runs whole super-steps of 64 k, two of them in flight
+    if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
     k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile

@@ -119,6 +119,7 @@ def test_heuristic_choices():
     assert binding.describe_config("linear", 8192, 8192, 8192).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("ffn", 8192, 14336, 4096).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("linear", 8192, 8192, 64).endswith("KERNEL=gemm_nt_pipe")
+    assert binding.describe_config("linear", 8192, 8192, 8200).endswith("KERNEL=gemm_nt_pipe")
     assert binding.describe_config("matmul", 8192, 8192, 8192, "nn").endswith("KERNEL=gemm_persistent")
     assert binding.describe_config("ffn", 8192, 14336, 4096).startswith("BM=256,BN=256")
     small = binding.describe_config("matmul", 256, 256, 256, "nn")

@@ -26,6 +26,9 @@ pytestmark = pytest.mark.gpu
 
 CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
+    # a small persistent grid: several tiles per workgroup, K direction
+    # alternating between them, prefetch running across tile boundaries
+    "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     "BM=256,BN=256,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=2",
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=1",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
@@ -33,6 +36,10 @@ CONFIGS = [
 ]
 FFN_CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
+    "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
+    # a small persistent grid: several tiles per workgroup, K direction
+    # alternating between them, prefetch running across tile boundaries
+    "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     "BM=256,BN=256,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=2",
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=1",
     "BM=128,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1",
@@ -101,7 +108,10 @@ def shapes_for(layout):
     """(M, N, K) spanning several tiles with ragged tails; contiguous extents
     stay multiples of 8 as the ABI requires (A's rows are M long for TN/TT,
     B's rows are N long for NN/TN)."""
-    base = [(1, 8, 8), (17, 24, 72), (129, 136, 64), (300, 264, 200), (520, 392, 4104)]
+    # the last three have K a multiple of 64 (>= 128), the whole-line slab
+    # kernel's domain; the others take the 32-k pipeline or the basic kernel
+    base = [(1, 8, 8), (17, 24, 72), (129, 136, 64), (300, 264, 200), (520, 392, 4104),
+            (257, 520, 128), (300, 264, 192), (520, 392, 4160)]
     out = []
     for M, N, K in base:
         if layout in ("tn", "tt"):
@@ -110,6 +120,16 @@ def shapes_for(layout):
             N = N + 3
         out.append((M, N, K))
     return out
+
+
+def test_slab_shapes_select_slab_kernel():
+    binding.set_config(CONFIGS[0])
+    try:
+        for (M, N, K) in shapes_for("nt")[-3:]:
+            assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_nt_slab")
+        assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
+    finally:
+        binding.set_config(None)
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
@@ -133,7 +153,7 @@ def test_mapping_bitexact_linear_bias(dev, cfg, layout):
 @pytest.mark.parametrize("layout", ["nn", "nt", "tn", "tt"])
 def test_mapping_bitexact_matmul_f32(dev, cfg, layout):
     binding.set_config(cfg)
-    for (M, N, K) in shapes_for(layout)[:4] + [(264, 136, 2056)]:
+    for (M, N, K) in shapes_for(layout)[:4] + [(264, 136, 2056), (264, 136, 2112)]:
         say("mapping matmul f32", layout, cfg, (M, N, K))
         A, B = synth.dense_int_operands(M, N, K, layout, seed=M + N + K)
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -146,7 +166,8 @@ def test_mapping_bitexact_matmul_f32(dev, cfg, layout):
 @pytest.mark.parametrize("cfg", FFN_CONFIGS)
 def test_mapping_bitexact_ffn(dev, cfg):
     binding.set_config(cfg)
-    for (M, N, K) in [(1, 3, 8), (130, 200, 72), (300, 515, 264), (520, 264, 1032)]:
+    for (M, N, K) in [(1, 3, 8), (130, 200, 72), (300, 515, 264), (520, 264, 1032), (300, 515, 256),
+                      (520, 264, 1088)]:
         say("mapping ffn glu_identity", cfg, (M, N, K))
         ops = synth.mapping_operands(M, N, K, "nt", seed=M + 5 * N + K, gated=True)
         x, Wg, Wu = ops["A"], ops["B"], ops["B2"]
@@ -162,9 +183,10 @@ def test_mapping_bitexact_ffn(dev, cfg):
 # ------------------------------------------------------------ numerics
 @pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("epi", ["none", "bias", "gelu_tanh", "bias_gelu_tanh"])
-def test_linear_epilogues_random(dev, cfg, epi):
+@pytest.mark.parametrize("K", [520, 512])
+def test_linear_epilogues_random(dev, cfg, epi, K):
     binding.set_config(cfg)
-    M, N, K = 333, 270, 520
+    M, N = 333, 270
     say("linear random", epi, cfg)
     x = synth.randn_bf16((M, K), 1.0, 1)
     W = synth.randn_bf16((N, K), K ** -0.5, 2)
@@ -176,9 +198,10 @@ def test_linear_epilogues_random(dev, cfg, epi):
 
 
 @pytest.mark.parametrize("cfg", FFN_CONFIGS)
-def test_ffn_swiglu_random(dev, cfg):
+@pytest.mark.parametrize("K", [264, 256])
+def test_ffn_swiglu_random(dev, cfg, K):
     binding.set_config(cfg)
-    M, N, K = 300, 390, 264
+    M, N = 300, 390
     say("ffn swiglu random", cfg)
     x = synth.randn_bf16((M, K), 1.0, 4)
     Wg = synth.randn_bf16((N, K), K ** -0.5, 5)
@@ -276,10 +299,11 @@ def test_unaligned_output_rows_and_pointer(dev):
 
 
 @pytest.mark.parametrize("cfg", CONFIGS[:2])
-def test_guard_bands_untouched(dev, cfg):
+@pytest.mark.parametrize("K", [200, 192])
+def test_guard_bands_untouched(dev, cfg, K):
     binding.set_config(cfg)
-    M, N, K = 259, 261, 200
-    say("guard bands", cfg)
+    M, N = 259, 261
+    say("guard bands", cfg, K)
     guard = 2048  # elements = 4 KiB of fp32
     A, B = synth.dense_int_operands(M, N, K, "nt", seed=5)
     buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device=dev)
