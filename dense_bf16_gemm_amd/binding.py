@@ -23,6 +23,7 @@ GLU_ACTS = {"silu": 0, "identity": 1}
 EXPORTS = (
     "mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
     "mm_describe_config", "mm_debug_schedule", "mm_status_string", "mm_last_error",
+    "mm_workspace_size", "mm_matmul_ws", "mm_linear_ws",
 )
 
 _lib = None
@@ -49,12 +50,16 @@ def load(path: str = LIB_PATH):
     lib.mm_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.mm_ffn_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.mm_ffn_glu.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.mm_workspace_size.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(ctypes.c_int64)]
+    lib.mm_matmul_ws.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp, i64, vp]
+    lib.mm_linear_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp, i64, vp]
     lib.mm_set_config.argtypes = [ctypes.c_char_p]
     lib.mm_describe_config.argtypes = [ci, i64, i64, i64, ci, ctypes.c_char_p, i64]
     lib.mm_debug_schedule.argtypes = [ci, i64, i64, i64, ci, i64, ctypes.POINTER(ctypes.c_int32), i64,
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
-                 "mm_describe_config", "mm_debug_schedule"):
+                 "mm_describe_config", "mm_debug_schedule", "mm_workspace_size", "mm_matmul_ws",
+                 "mm_linear_ws"):
         getattr(lib, name).restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p
@@ -74,6 +79,15 @@ def check(status: int, what: str) -> None:
 def set_config(spec: Optional[str]) -> None:
     """Replaces the tile-configuration heuristic (None/"" restores it)."""
     check(load().mm_set_config(spec.encode() if spec else None), "mm_set_config")
+
+
+def workspace_size(form: str, M: int, N: int, K: int, layout: str = "nt") -> int:
+    """Bytes of split-K workspace a call of this shape may use on the current
+    device (0: none)."""
+    n = ctypes.c_int64(0)
+    check(load().mm_workspace_size(1 if form == "ffn" else 0, M, N, K, LAYOUTS[layout],
+                                   ctypes.byref(n)), "mm_workspace_size")
+    return n.value
 
 
 def describe_config(form: str, M: int, N: int, K: int, layout: str = "nt") -> str:

@@ -77,6 +77,14 @@ struct GemmParams {
   int group_m;           // band height of the grouped tile order, in tiles
   int xcd_remap;
   int k_alt;             // alternate K direction per persistent tile
+  // Split-K (gemm_nt_slab with SPLITK): work unit u = s * num_tiles + t runs
+  // super-steps [s*KS/S, (s+1)*KS/S) of tile t.  Slices 0..S-2 leave fp32
+  // partial tiles in the workspace and raise a flag; slice S-1 waits for them,
+  // adds them in slice order and runs the epilogue.
+  int sk_slices;         // S (1 = off)
+  uint32_t sk_epoch;     // flag value of this launch (never 0)
+  float* sk_part;        // [num_tiles][S-1][256*256] partial tiles
+  uint32_t* sk_flag;     // [num_tiles][S-1]
 };
 
 // Schedule helpers, shared with the host so that it can describe the order.

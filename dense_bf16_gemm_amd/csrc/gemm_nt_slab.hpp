@@ -50,9 +50,10 @@ __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
 }
 
-template <int BM, int BN, int WGM, int WGN, bool FFN>
+template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
+  static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;
   constexpr int WTN = BN / WGN;
@@ -77,8 +78,11 @@ gemm_nt_slab(GemmParams p) {
   // wave-uniform results back to scalar registers, so that all descriptor
   // and offset arithmetic below stays scalar)
   const int wg = __builtin_amdgcn_readfirstlane(remap_workgroup(blockIdx.x, G, p.xcd_remap));
-  if (wg >= p.num_tiles) return;
-  const int my_tiles = __builtin_amdgcn_readfirstlane((p.num_tiles - wg + G - 1) / G);
+  // work units: tiles, or (split-K) tile slices, slice-major
+  const int S = SPLITK ? p.sk_slices : 1;
+  const int units = p.num_tiles * S;
+  if (wg >= units) return;
+  const int my_tiles = __builtin_amdgcn_readfirstlane((units - wg + G - 1) / G);
   const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
   const int M = p.M, N = p.N, K = p.K;
   const int64_t ld = K;
@@ -100,10 +104,26 @@ gemm_nt_slab(GemmParams p) {
     uint64_t a_base, b0_base, b1_base;
     uint32_t a_rec, b_rec;
     int alt;
+    int kbeg;  // first super-step of a split-K slice (0 otherwise)
+  };
+  // output tile, split-K slice, and first and count of super-steps of unit u
+  auto unit_of = [&](int u, int* tile, int* slice, int* kbeg, int* nks) __attribute__((always_inline)) {
+    *tile = u;
+    *slice = 0;
+    *kbeg = 0;
+    *nks = KS;
+    if constexpr (SPLITK) {
+      *slice = __builtin_amdgcn_readfirstlane(u / p.num_tiles);
+      *tile = u - *slice * p.num_tiles;
+      *kbeg = __builtin_amdgcn_readfirstlane(*slice * KS / S);
+      *nks = __builtin_amdgcn_readfirstlane((*slice + 1) * KS / S) - *kbeg;
+    }
   };
   auto tile_desc = [&](int tile_i) __attribute__((always_inline)) {
     int tm, tn;
-    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    int tile, slice, kbeg, nks;
+    unit_of(wg + tile_i * G, &tile, &slice, &kbeg, &nks);
+    tile_coords(tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int m0 = tm * BM;
@@ -116,7 +136,8 @@ gemm_nt_slab(GemmParams p) {
     d.b_rec = (uint32_t)nrows * row_bytes;
     d.b0_base = reinterpret_cast<uint64_t>(p.B + (int64_t)n0 * ld);
     d.b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + (int64_t)n0 * ld) : d.b0_base;
-    d.alt = p.k_alt && (tile_i & 1);
+    d.alt = SPLITK ? 0 : (p.k_alt && (tile_i & 1));
+    d.kbeg = kbeg;
     return d;
   };
   TileDesc cur = tile_desc(0);
@@ -149,6 +170,7 @@ gemm_nt_slab(GemmParams p) {
   };
   // first k of super-step ks of the fetched tile
   auto k0_of = [&](int ks) __attribute__((always_inline)) {
+    if constexpr (SPLITK) return (cur.kbeg + ks) * kSlabK;
     const int alt = __builtin_amdgcn_readfirstlane(cur.alt);
     return (alt ? (KS - 1 - ks) : ks) * kSlabK;
   };
@@ -386,26 +408,126 @@ gemm_nt_slab(GemmParams p) {
     }
   };
 
+  // Split-K end of a work unit (plain product, no epilogue math), one code
+  // path for every slice: slices 0..S-2 (partial) write their raw fp32 tile
+  // into a 256 x 256 row-major workspace slot; the last slice adds the nadd
+  // slots at `addend` in slot order and writes the output (bounds-checked).
+  auto epilogue_sk = [&](bool partial, float* slot, int m0, int n0, const float* addend, int nadd)
+      __attribute__((always_inline)) {
+    const int ldo = partial ? 256 : N;
+    const int mlim = partial ? 256 : M - m0, nlim = partial ? 256 : N - n0;
+    const bool o_f32 = partial || p.out_f32;
+    char* obase = partial ? reinterpret_cast<char*>(slot)
+                          : reinterpret_cast<char*>(p.out) + ((int64_t)m0 * N + n0) * (o_f32 ? 4 : 2);
+    const bool vec_ok = partial || p.out_vec;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        const int ml = wrow_a + lx + 16 * fm;      // tile-local row
+        const int nl = wrow_b + 32 * pr + 8 * lk;  // tile-local first column
+        // the other slices' sums first, then this slice's accumulators (the
+        // accumulators are read at their point of use, which keeps the
+        // compiler from moving them out of their registers early)
+        __builtin_amdgcn_sched_barrier(0);
+        float add[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) add[j] = 0.f;
+        const float* a = addend + ml * 256 + nl;
+        for (int s2 = 0; s2 < nadd; ++s2, a += 65536) {
+          const f32x4 x0 = reinterpret_cast<const f32x4*>(a)[0];
+          const f32x4 x1 = reinterpret_cast<const f32x4*>(a)[1];
+          add[0] += x0[0]; add[1] += x0[1]; add[2] += x0[2]; add[3] += x0[3];
+          add[4] += x1[0]; add[5] += x1[1]; add[6] += x1[2]; add[7] += x1[3];
+        }
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = acc[fm][2 * pr + (j >> 2)][j & 3] + add[j];
+        if (ml < mlim) {
+          const int64_t e = (int64_t)ml * ldo + nl;
+          if (o_f32) {
+            float* o = reinterpret_cast<float*>(obase) + e;
+            if (vec_ok && nl + 8 <= nlim) {
+              reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
+              reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (nl + j < nlim) o[j] = v[j];
+            }
+          } else {
+            uint16_t* o = reinterpret_cast<uint16_t*>(obase) + e;
+            if (vec_ok && nl + 8 <= nlim) {
+              u32x4 w;
+              w[0] = pack_bf16x2(v[0], v[1]);
+              w[1] = pack_bf16x2(v[2], v[3]);
+              w[2] = pack_bf16x2(v[4], v[5]);
+              w[3] = pack_bf16x2(v[6], v[7]);
+              *reinterpret_cast<u32x4*>(o) = w;
+            } else {
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (nl + j < nlim) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
+            }
+          }
+        }
+      }
+    }
+  };
+
   for (int tile_i = 0; tile_i < my_tiles; ++tile_i) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The copies of super-step ks fetch this tile's super-step ks + 2, and
-    // from ks = KS - 2 on the next tile's super-steps 0 and 1.
+    // The copies of super-step ks fetch this unit's super-step ks + 2, and
+    // from ks = nks - 2 on the next unit's super-steps 0 and 1.
     const TileDesc nxt = tile_desc(tile_i + 1 < my_tiles ? tile_i + 1 : tile_i);
+    int h_tile, h_slice, h_kbeg, nks;
+    unit_of(wg + tile_i * G, &h_tile, &h_slice, &h_kbeg, &nks);
     __builtin_amdgcn_s_waitcnt(kLgkmDrained);
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < nks; ++ks) {
       int lks = ks + 2;
-      if (lks >= KS) {
-        lks -= KS;
+      if (lks >= nks) {
+        lks -= nks;
         cur = nxt;
       }
       super_step(k0_of(lks));
     }
+    if constexpr (SPLITK) {
+      // Slices 0..S-2 leave their raw tile in slot (tile, slice) and raise
+      // its flag; the last slice waits (bounded) for the flags and adds the
+      // slots in slice order.  Release/acquire fences at device scope make
+      // the slots written on one XCD visible on another.
+      constexpr int64_t kSlot = 256 * 256;
+      const int nslot = S - 1;
+      const bool partial = h_slice < nslot;
+      float* slots = p.sk_part + (int64_t)h_tile * nslot * kSlot;
+      if (!partial && tid == 0) {
+        for (int s2 = 0; s2 < nslot; ++s2) {
+          const uint32_t* f = p.sk_flag + h_tile * nslot + s2;
+          for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.sk_epoch) break;
+            __builtin_amdgcn_s_sleep(8);
+          }
+        }
+      }
+      __builtin_amdgcn_s_barrier();
+      if (!partial) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      int tm, tn;
+      tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+      epilogue_sk(partial, slots + (int64_t)h_slice * kSlot, tm * BM, tn * OUT_BN, slots,
+                  partial ? 0 : nslot);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_s_barrier();
+      if (partial && tid == 0)
+        __hip_atomic_store(p.sk_flag + h_tile * nslot + h_slice, p.sk_epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
 
     int tm, tn;
-    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * OUT_BN;
     using T = std::true_type;
     using F = std::false_type;

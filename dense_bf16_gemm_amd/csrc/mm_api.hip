@@ -43,6 +43,7 @@ struct KernelEntry {
              // 1: K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
   const void* fn;
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
+  bool splitk = false;         // gemm_nt_slab<..., SPLITK>: needs a workspace
 };
 
 #define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
@@ -61,11 +62,16 @@ struct KernelEntry {
   {256, 256, 2, 2, true, true, FFN, 3,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, FFN>), {0}}
 
+#define MM_KSK()                                                                           \
+  {256, 256, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true>), {0}, true}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
+    MM_KSK(),
     MM_KS(false),
     MM_KS(true),
     MM_KPP(false),
@@ -88,10 +94,11 @@ KernelEntry g_kernels[] = {
 };
 constexpr int kNumKernels = sizeof(g_kernels) / sizeof(g_kernels[0]);
 
-KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe) {
+KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe,
+                         bool splitk = false) {
   for (auto& k : g_kernels)
     if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
-        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe)
+        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk)
       return &k;
   return nullptr;
 }
@@ -106,6 +113,7 @@ struct Config {
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
   int pipe = 3;   // preferred kernel family: 3 slab ring, 2 ping-pong, 1 pipeline, 0 basic
+  int sk = 0;     // split-K slices when a workspace is given: 0 automatic, 1 off, n forced
 };
 
 std::mutex g_cfg_mu;
@@ -138,9 +146,10 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "KALT") c.kalt = (int)v;
     else if (key == "GRID") c.grid = (int)v;
     else if (key == "PIPE") c.pipe = (int)v;
+    else if (key == "SK") c.sk = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 3) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 3 || c.sk > 64) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -259,6 +268,8 @@ struct Request {
   int epi;  // mmk::EPI_*
   bool out_f32;
   bool ffn;
+  void* ws = nullptr;     // caller's workspace (split-K), may be null
+  int64_t ws_bytes = 0;
 };
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -296,6 +307,11 @@ mm_status validate(const Request& r) {
       (r.ffn && overlaps(r.out, ob, r.B2, r.K * r.N * 2)) ||
       (need_bias && overlaps(r.out, ob, r.bias, r.N * 2)))
     return fail(MM_ERR_INVALID_VALUE, "out overlaps an input");
+  if (r.ws_bytes < 0) return fail(MM_ERR_INVALID_VALUE, "negative workspace size");
+  if (r.ws && (overlaps(r.ws, r.ws_bytes, r.out, ob) || overlaps(r.ws, r.ws_bytes, r.A, r.M * r.K * 2) ||
+               overlaps(r.ws, r.ws_bytes, r.B, r.K * r.N * 2) ||
+               (need_bias && overlaps(r.ws, r.ws_bytes, r.bias, r.N * 2))))
+    return fail(MM_ERR_INVALID_VALUE, "workspace overlaps an operand or the output");
   return MM_OK;
 }
 
@@ -306,15 +322,73 @@ struct Plan {
   int threads;
 };
 
+// ----------------------------------------------------------------------------
+// Split-K: the pages name splitting the K loop over workgroups (split-K, and
+// stages spread over SMs "a la stream-K") and leave both out of their
+// persistent scheduler (PR "Implement persistent matmul scheduling", review
+// notes).  Here: when a K-contiguous single-weight product has fewer 256 x 256
+// tiles than the grid has workgroups, the slab kernel's K loop is cut into S
+// slices and the units (slice, tile) are spread over the grid; the partial
+// tiles meet in a caller-provided workspace.
+// ----------------------------------------------------------------------------
+constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
+
+// plain K-contiguous products (no bias or activation: the slices' sums meet
+// before any epilogue math would apply)
+bool splitk_shape(const Request& r) {
+  return !r.ffn && r.epi == mmk::EPI_NONE && r.layout == MM_NT && r.K % mmk::kSlabK == 0 &&
+         r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31);
+}
+
+// Slices for a grid of `wgs` resident workgroups (1 = no split).
+int splitk_slices(const Request& r, const Config& c, int64_t wgs) {
+  if (c.sk == 1 || !splitk_shape(r)) return 1;
+  const int64_t T = cdiv(r.M, 256) * cdiv(r.N, 256);
+  const int64_t KS = r.K / mmk::kSlabK;
+  if (c.sk >= 2) return KS / c.sk >= 2 ? c.sk : 1;
+  if (T >= wgs) return 1;
+  // Fewest slices that occupy three quarters of the grid: more slices read
+  // the operands from more places at once and were slower (2047 x 3001 x
+  // 65536, 96 tiles on 256 CUs: 2 slices 745 us, 4: 941, 5: 849, 8: 948,
+  // 16: 1287; unsplit 1165).
+  int S = (int)cdiv(3 * wgs, 4 * T);
+  if (S < 2) S = 2;
+  if (S > 16) S = 16;
+  while (S > 2 && KS / S < 8) --S;
+  return KS / S >= 2 ? S : 1;
+}
+
+int64_t splitk_ws_bytes(const Request& r, int S) {
+  if (S <= 1) return 0;
+  const int64_t slots = cdiv(r.M, 256) * cdiv(r.N, 256) * (S - 1);
+  const int64_t flags = cdiv(slots * 4, 256) * 256;
+  return flags + slots * kSkSlotBytes;
+}
+
+// Work units of a split-K launch run on this many workgroups, all resident
+// at once (a last slice waits for the others).
+int64_t splitk_wgs(const Config& c, int cus, int occ) {
+  const int64_t resident = (int64_t)cus * occ;
+  return c.grid > 0 && c.grid < resident ? c.grid : resident;
+}
+
+std::atomic<uint32_t> g_sk_epoch{0};
+
 // Everything but the device-dependent grid size; no HIP calls.
-mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
+mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
   if (r.ffn && !b_kc) return fail(MM_ERR_UNSUPPORTED, "FFN weights must be [N][K]");
+  Config c = c_in;
   KernelEntry* k = nullptr;
+  if (S > 1) {
+    c.bm = c.bn = 256;
+    c.wgm = c.wgn = 2;
+    k = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
+  }
   // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
-  for (int fam = c.pipe; fam >= 0 && !k; --fam) {
+  for (int fam = c.pipe; fam >= 0 && !k && S <= 1; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
     // the slab kernel runs whole super-steps of 64 k, two of them in flight
     if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
@@ -352,6 +426,14 @@ mm_status plan_host(const Request& r, const Config& c, Plan* pl) {
   p.group_m = c.group;
   p.xcd_remap = c.xcd;
   p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
+  p.sk_slices = 1;
+  if (S > 1) {
+    p.k_alt = 0;
+    p.sk_slices = S;
+    const int64_t slots = (int64_t)p.num_tiles * (S - 1);
+    p.sk_flag = static_cast<uint32_t*>(r.ws);
+    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + cdiv(slots * 4, 256) * 256);
+  }
   pl->kernel = k;
   pl->threads = k->wgm * k->wgn * 64;  // the selected kernel's block size
   pl->grid = 0;
@@ -368,14 +450,32 @@ mm_status run(const Request& r, void* stream) {
   if (s != MM_OK) return s;
   int cus = 0, occ = 0;
   if ((s = device_cus(&cus)) != MM_OK) return s;
+  if (r.ws && splitk_shape(r) && c.sk != 1) {
+    // the split-K kernel's grid: one wave of resident workgroups
+    int sk_occ = 0;
+    KernelEntry* sk = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
+    if ((s = kernel_occupancy(sk, &sk_occ)) != MM_OK) return s;
+    const int S = splitk_slices(r, c, splitk_wgs(c, cus, sk_occ));
+    if (S > 1) {
+      if (r.ws_bytes < splitk_ws_bytes(r, S))
+        return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
+      if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+      if ((s = plan_host(r, c, &pl, S)) != MM_OK) return s;
+      uint32_t e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+      if (e == 0) e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+      pl.p.sk_epoch = e;
+    }
+  }
   if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
+  const int64_t units = (int64_t)pl.p.num_tiles * pl.p.sk_slices;
   int64_t grid = c.grid > 0 ? c.grid : (int64_t)cus * occ;
-  if (grid > pl.p.num_tiles) grid = pl.p.num_tiles;
+  if (pl.p.sk_slices > 1 && grid > (int64_t)cus * occ) grid = (int64_t)cus * occ;
+  if (grid > units) grid = units;
   if (std::getenv("MM_LOG"))
     std::fprintf(stderr, "libmm: M=%lld N=%lld K=%lld layout=%d ffn=%d -> BM=%d BN=%d WM=%d WN=%d G=%d "
-                 "XCD=%d KALT=%d grid=%lld tiles=%d\n", (long long)r.M, (long long)r.N,
+                 "XCD=%d KALT=%d grid=%lld tiles=%d slices=%d\n", (long long)r.M, (long long)r.N,
                  (long long)r.K, r.layout, (int)r.ffn, c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd,
-                 pl.p.k_alt, (long long)grid, pl.p.num_tiles);
+                 pl.p.k_alt, (long long)grid, pl.p.num_tiles, pl.p.sk_slices);
   void* args[] = {&pl.p};
   hipError_t e = hipLaunchKernel(pl.kernel->fn, dim3((unsigned)grid), dim3(pl.threads), args, 0,
                                  static_cast<hipStream_t>(stream));
@@ -413,6 +513,49 @@ mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, i
   const int e = map_epilogue(epi);
   if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
   Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  return run(r, stream);
+}
+
+mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
+                            int64_t* bytes) {
+  g_last_error.clear();
+  if (!bytes || (form != 0 && form != 1) || M < 0 || N < 0 || K < 0 || layout < MM_NN ||
+      layout > MM_TT)
+    return fail(MM_ERR_INVALID_VALUE, "bad arguments");
+  *bytes = 0;
+  Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
+            false, form == 1};
+  if (M == 0 || N == 0 || K == 0 || !splitk_shape(r)) return MM_OK;
+  const Config c = choose_config(r.ffn, M, N, K);
+  if (c.sk == 1) return MM_OK;
+  int cus = 0, occ = 0;
+  mm_status s;
+  if ((s = device_cus(&cus)) != MM_OK) return s;
+  if ((s = kernel_occupancy(find_kernel(256, 256, 2, 2, true, true, false, 3, true), &occ)) != MM_OK)
+    return s;
+  *bytes = splitk_ws_bytes(r, splitk_slices(r, c, splitk_wgs(c, cus, occ)));
+  return MM_OK;
+}
+
+mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
+                       mm_layout layout, mm_out_dtype out_dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (out_dtype != MM_OUT_BF16 && out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_INVALID_VALUE, "bad output dtype");
+  Request r{A, B, nullptr, nullptr, out, M, N, K, (int)layout, mmk::EPI_NONE,
+            out_dtype == MM_OUT_F32, false, workspace, workspace ? workspace_bytes : 0};
+  return run(r, stream);
+}
+
+mm_status mm_linear_ws(const void* x, const void* W, const void* bias, void* out, int64_t M,
+                       int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  const int e = map_epilogue(epi);
+  if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
+  Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false, workspace,
+            workspace ? workspace_bytes : 0};
   return run(r, stream);
 }
 

@@ -39,10 +39,45 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+# One zero-filled split-K workspace per device, grown on demand.  Calls on one
+# stream may share it (each launch stamps it with a fresh number); calls in
+# flight on different streams at once must pass their own.
+_workspaces: dict = {}
+
+
+def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _resolve_ws(workspace, form: str, M: int, N: int, K: int, layout: str, device):
+    """(pointer, bytes) of the split-K workspace: "auto" uses the per-device
+    one sized by mm_workspace_size, None disables split-K, a uint8 tensor is
+    used as given."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 tensor')
+        nbytes = binding.workspace_size(form, M, N, K, layout) if M and N and K else 0
+        if nbytes == 0:
+            return None, 0
+        workspace = _workspace(nbytes, device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+    return workspace.data_ptr(), workspace.numel()
+
+
 def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+           out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """MatmulOp form: out = A @ B with A [M,K] and B [K,N] (either may be a
-    transposed view), fp32 accumulation, bf16 or fp32 output."""
+    transposed view), fp32 accumulation, bf16 or fp32 output.  `workspace`
+    enables split-K for shapes with too few output tiles (see
+    mm_workspace_size): "auto", None (off) or a zero-filled uint8 tensor."""
     _check(A, "A")
     _check(B, "B")
     M, K = A.shape
@@ -57,16 +92,21 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype = torch.bflo
     elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
     lib = binding.load()
-    st = lib.mm_matmul(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, binding.LAYOUTS[layout],
-                       binding.OUT_DTYPES["f32" if out_dtype == torch.float32 else "bf16"], _stream())
-    binding.check(st, "mm_matmul")
+    wp, wb = _resolve_ws(workspace, "matmul", M, N, K, layout, A.device)
+    st = lib.mm_matmul_ws(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,
+                          binding.LAYOUTS[layout],
+                          binding.OUT_DTYPES["f32" if out_dtype == torch.float32 else "bf16"], wp, wb,
+                          _stream())
+    binding.check(st, "mm_matmul_ws")
     return out
 
 
 def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None,
-           epilogue: str = "none", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+           epilogue: str = "none", out: Optional[torch.Tensor] = None,
+           workspace="auto") -> torch.Tensor:
     """LinearOp form: out = epi(x @ W.T + bias) with x [M,K], W [N,K], bias [N],
-    epilogue one of none | bias | gelu_tanh | bias_gelu_tanh; bf16 output."""
+    epilogue one of none | bias | gelu_tanh | bias_gelu_tanh; bf16 output.
+    `workspace` as for matmul (split-K applies to epilogue "none" only)."""
     _check(x, "x")
     _check(W, "W")
     M, K = x.shape
@@ -87,10 +127,12 @@ def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None
     elif out.shape != (M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [M, N] tensor")
     lib = binding.load()
-    st = lib.mm_linear(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
-                       out.data_ptr(), M, N, K, binding.LAYOUTS[layout], binding.EPILOGUES[epilogue],
-                       _stream())
-    binding.check(st, "mm_linear")
+    wp, wb = (_resolve_ws(workspace, "linear", M, N, K, layout, x.device) if epilogue == "none"
+              else (None, 0))
+    st = lib.mm_linear_ws(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
+                          out.data_ptr(), M, N, K, binding.LAYOUTS[layout],
+                          binding.EPILOGUES[epilogue], wp, wb, _stream())
+    binding.check(st, "mm_linear_ws")
     return out
 
 

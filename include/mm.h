@@ -104,6 +104,38 @@ mm_status mm_matmul(const void* A, const void* B, void* out, int64_t M, int64_t 
 mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, int64_t M,
                     int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* stream);
 
+/* Split-K workspace (PR "Implement persistent matmul scheduling", review
+ * notes: splitting the K loop over workgroups, split-K and stream-K, named
+ * there and left out of the persistent scheduler).  When a plain K-contiguous
+ * (MM_NT) product -- mm_matmul, or mm_linear with MM_EPI_NONE -- with K a
+ * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
+ * workgroups, the _ws entry points below cut each tile's K loop into slices
+ * spread over the grid; the fp32 partial tiles meet in this workspace.
+ *   form    0 matmul/linear, 1 FFN (never uses a workspace)
+ *   bytes   receives the size a call of this shape on the current device may
+ *           use; 0 = the shape runs without one.  Queries the device (CU
+ *           count, occupancy); launches nothing.
+ * Workspace contract: device memory, 256-byte aligned, zero-filled before its
+ * first use, reusable by later calls on the same stream; two calls in flight
+ * at once must not share it, and a captured graph must not replay a call that
+ * uses one (each call stamps it with a fresh launch number).               */
+mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
+                            int64_t* bytes);
+
+/* mm_matmul / mm_linear with a workspace (see mm_workspace_size).  With a NULL
+ * workspace, or a shape that needs none, they behave exactly as mm_matmul /
+ * mm_linear.  A workspace smaller than reported returns MM_ERR_INVALID_VALUE;
+ * one that overlaps an operand or the output returns MM_ERR_INVALID_VALUE.
+ * Still one kernel per call; the slices' partial sums are added in slice
+ * order, so results are reproducible run to run (they differ from the
+ * unsplit kernel's by fp32 rounding order only).                           */
+mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
+                       mm_layout layout, mm_out_dtype out_dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+mm_status mm_linear_ws(const void* x, const void* W, const void* bias, void* out, int64_t M,
+                       int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
 /* Llama-FFN horizontal fusion in one kernel:
  *   out[M][N] = SiLU(x . W_gate^T) * (x . W_up^T), bf16 output (RNE),
  * x [M][K], W_gate and W_up [N][K].  Each x tile is loaded once and feeds
@@ -120,7 +152,10 @@ mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* 
  * (BM/BN: output tile; WM/WN: wave grid; G: grouped-swizzle band height in
  * tiles; XCD: XCD-aware workgroup remap on/off; KALT: alternate the K
  * direction per persistent tile (1), never (0) or automatically (2);
- * GRID: persistent grid size, 0 = one wave of resident workgroups).  The
+ * GRID: persistent grid size, 0 = one wave of resident workgroups; PIPE:
+ * preferred kernel family, 3 whole-line slab ring, 2 ping-pong, 1 32-k
+ * pipeline, 0 basic; SK: split-K slices when a workspace is given, 0
+ * automatic, 1 never, n >= 2 forced).  The
  * heuristic is replaced for every later call in the process, in the manner
  * of the pages' heuristic plugin (PR "Translate MmaOp patterns properly on
  * Hopper", review of MatmulSchedulerPluginTest).  NULL or "" restores the

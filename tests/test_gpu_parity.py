@@ -163,6 +163,91 @@ def test_mapping_bitexact_matmul_f32(dev, cfg, layout):
         np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
+# ------------------------------------------------------------ split-K
+# (M, N, K, configuration): few 256 x 256 output tiles, long K.  The forced
+# slice counts with small grids make slices wait on other workgroups across
+# rounds of work units.
+SK_CASES = [
+    (520, 395, 8192, None),
+    (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=4"),
+    (257, 520, 1024, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=0,KALT=2,SK=2,GRID=2"),
+    (64, 8, 4096, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=7"),
+]
+
+
+def call_matmul_ws(A, B, M, N, K, out_f32, out, ws, nbytes):
+    lib = binding.load()
+    st = lib.mm_matmul_ws(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, binding.LAYOUTS["nt"],
+                          1 if out_f32 else 0, ws.data_ptr() if ws is not None else None, nbytes,
+                          stream())
+    binding.check(st, "mm_matmul_ws")
+
+
+@pytest.mark.parametrize("case", range(len(SK_CASES)))
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_splitk_mapping_bitexact(dev, case, out_f32):
+    """Integer operands keep every partial sum exact, so the slices' sums,
+    added in any order, must give the oracle's bits."""
+    M, N, K, cfg = SK_CASES[case]
+    binding.set_config(cfg)
+    try:
+        nbytes = binding.workspace_size("matmul", M, N, K)
+        say("split-K mapping", (M, N, K), cfg, "f32" if out_f32 else "bf16", nbytes)
+        assert nbytes > 0, "this shape should take the split-K path"
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        A, B = synth.dense_int_operands(M, N, K, "nt", seed=M + 3 * N + K)
+        A, B = A.to(dev), B.to(dev)
+        ref, bits = oracle.gemm(synth.bits(A.cpu()), synth.bits(B.cpu()), "nt")
+        out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
+        for rep in range(3):  # the same workspace again: fresh launch numbers each time
+            out.fill_(float("nan"))
+            call_matmul_ws(A, B, M, N, K, out_f32, out, ws, nbytes)
+            torch.cuda.synchronize()
+            if out_f32:
+                np.testing.assert_array_equal(out.cpu().numpy(), ref)
+            else:
+                np.testing.assert_array_equal(to_bits(out), bits)
+    finally:
+        binding.set_config(None)
+
+
+def test_splitk_random_and_fallbacks(dev):
+    M, N, K = 700, 900, 16384
+    x = synth.randn_bf16((M, K), 1.0, 11).to(dev)
+    W = synth.randn_bf16((N, K), 2.0 ** -7, 12).to(dev)
+    say("split-K random", (M, N, K))
+    nbytes = binding.workspace_size("matmul", M, N, K)
+    assert nbytes > 0
+    y, _ = oracle.gemm(synth.bits(x.cpu()), synth.bits(W.cpu()), "nt")
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    call_matmul_ws(x, W.t(), M, N, K, True, out, ws, nbytes)
+    torch.cuda.synchronize()
+    assert tol_excess(out.cpu().numpy(), y, 1e-3) <= 0
+    # run to run identical (slices are added in a fixed order)
+    out2 = torch.empty_like(out)
+    call_matmul_ws(x, W.t(), M, N, K, True, out2, ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    # no workspace: the unsplit kernel, same tolerance
+    out3 = torch.empty_like(out)
+    call_matmul_ws(x, W.t(), M, N, K, True, out3, None, 0)
+    torch.cuda.synchronize()
+    assert tol_excess(out3.cpu().numpy(), y, 1e-3) <= 0
+    # linear with epilogue "none" takes the same path (bf16 out)
+    got = mm.linear(x, W, None, "none")
+    torch.cuda.synchronize()
+    assert tol_excess(got.float().cpu().numpy(), y, 2e-2) <= 0
+    # a workspace smaller than reported is refused before any launch
+    with pytest.raises(binding.MMError) as e:
+        call_matmul_ws(x, W.t(), M, N, K, True, out3, ws, nbytes - 256)
+    assert e.value.status == binding.MM_ERR_INVALID_VALUE
+    # a workspace overlapping the output is refused
+    with pytest.raises(binding.MMError) as e:
+        call_matmul_ws(x, W.t(), M, N, K, True, out3, out3.view(torch.uint8), out3.numel() * 4)
+    assert e.value.status == binding.MM_ERR_INVALID_VALUE
+
+
 @pytest.mark.parametrize("cfg", FFN_CONFIGS)
 def test_mapping_bitexact_ffn(dev, cfg):
     binding.set_config(cfg)
