@@ -81,6 +81,12 @@ struct GemmParams {
   // super-steps [s*KS/S, (s+1)*KS/S) of tile t.  Slices 0..S-2 leave fp32
   // partial tiles in the workspace and raise a flag; slice S-1 waits for them,
   // adds them in slice order and runs the epilogue.
+  // Batched form: `batch` independent products; operand / output bases of
+  // entry b are b * stride elements past entry 0 (a stride of 0 broadcasts).
+  // The persistent loop walks batch * num_tiles units, unit u being tile
+  // u % num_tiles of entry u / num_tiles.
+  int batch;             // >= 1
+  int64_t stride_a, stride_b, stride_out;
   int sk_slices;         // S (1 = off)
   uint32_t sk_epoch;     // flag value of this launch (never 0)
   float* sk_part;        // [num_tiles][S-1][256*256] partial tiles
@@ -93,6 +99,28 @@ __host__ __device__ inline int remap_workgroup(int b, int G, int on) {
   const int per = G / kNumXcd, rem = G % kNumXcd;
   const int xcd = b % kNumXcd, local = b / kNumXcd;
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Entry of the batched form that persistent unit u belongs to, its tile
+// index inside the entry, and the entry's operand and output bases.
+struct BatchView {
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* B2;
+  void* out;
+  int tile;
+};
+__device__ __forceinline__ BatchView batch_view(const GemmParams& p, int u) {
+  BatchView v{p.A, p.B, p.B2, p.out, u};
+  if (p.batch > 1) {
+    const int b = __builtin_amdgcn_readfirstlane(u / p.num_tiles);
+    v.tile = u - b * p.num_tiles;
+    v.A = p.A + (int64_t)b * p.stride_a;
+    v.B = p.B + (int64_t)b * p.stride_b;
+    v.B2 = p.B2 ? p.B2 + (int64_t)b * p.stride_b : nullptr;
+    v.out = static_cast<char*>(p.out) + (int64_t)b * p.stride_out * (p.out_f32 ? 4 : 2);
+  }
+  return v;
 }
 
 __host__ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int* tm,
@@ -264,8 +292,9 @@ gemm_persistent(GemmParams p) {
   const int wave_n = wave % WGN;
   const int G = gridDim.x;
   const int wg = remap_workgroup(blockIdx.x, G, p.xcd_remap);
-  if (wg >= p.num_tiles) return;
-  const int my_tiles = (p.num_tiles - wg + G - 1) / G;
+  const int units = p.num_tiles * p.batch;
+  if (wg >= units) return;
+  const int my_tiles = (units - wg + G - 1) / G;
   const int KT = p.k_tiles;
   const int total = my_tiles * KT;
 
@@ -287,7 +316,8 @@ gemm_persistent(GemmParams p) {
   // operands (into buffer `buf`), register loads for the others.
   auto issue_loads = [&](int tile_i, int kt, int buf) {
     int tm, tn;
-    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const BatchView bview = batch_view(p, wg + tile_i * G);
+    tile_coords(bview.tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int k0 = kstep_of(tile_i, kt) * kBK;
     const int m0 = tm * BM;
     const int n0 = tn * OUT_BN;
@@ -296,21 +326,21 @@ gemm_persistent(GemmParams p) {
       auto rowA = [&](int r) {
         int row = m0 + r;
         row = row < M ? row : M - 1;
-        return p.A + (int64_t)row * lda;
+        return bview.A + (int64_t)row * lda;
       };
       da.issue(rowA, stage, k0, K, wave, lane);
     } else {
-      sa.load(p.A, lda, m0, M, k0, K, tid);
+      sa.load(bview.A, lda, m0, M, k0, K, tid);
     }
     if constexpr (B_KC) {
       auto rowB = [&](int r) {
-        const uint16_t* base = p.B;
+        const uint16_t* base = bview.B;
         int row;
         if constexpr (FFN) {
           const int wb = r / WTN, within = r % WTN;
           const bool up = within >= WTN / 2;
           row = n0 + wb * (WTN / 2) + (up ? within - WTN / 2 : within);
-          base = up ? p.B2 : p.B;
+          base = up ? bview.B2 : bview.B;
         } else {
           row = n0 + r;
         }
@@ -319,7 +349,7 @@ gemm_persistent(GemmParams p) {
       };
       db.issue(rowB, stage + A_BYTES, k0, K, wave, lane);
     } else {
-      sb.load(p.B, ldb, n0, N, k0, K, tid);
+      sb.load(bview.B, ldb, n0, N, k0, K, tid);
     }
   };
 
@@ -386,7 +416,8 @@ gemm_persistent(GemmParams p) {
   // --- epilogue --------------------------------------------------------------
   auto epilogue = [&](int tile_i) {
     int tm, tn;
-    tile_coords(wg + tile_i * G, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const BatchView bview = batch_view(p, wg + tile_i * G);
+    tile_coords(bview.tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m_base = tm * BM + wrow_a + lx;
     const int g8 = 8 * lk;
     constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
@@ -425,7 +456,7 @@ gemm_persistent(GemmParams p) {
         }
         if (m >= M) continue;
         if (p.out_f32) {
-          float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * N + n;
+          float* o = reinterpret_cast<float*>(bview.out) + (int64_t)m * N + n;
           if (p.out_vec && n + 8 <= N) {
             reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
             reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
@@ -435,7 +466,7 @@ gemm_persistent(GemmParams p) {
               if (n + j < N) o[j] = v[j];
           }
         } else {
-          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m * N + n;
+          uint16_t* o = reinterpret_cast<uint16_t*>(bview.out) + (int64_t)m * N + n;
           if (p.out_vec && n + 8 <= N) {
             u32x4 w;
             w[0] = pack_bf16x2(v[0], v[1]);

@@ -80,7 +80,7 @@ gemm_nt_slab(GemmParams p) {
   const int wg = __builtin_amdgcn_readfirstlane(remap_workgroup(blockIdx.x, G, p.xcd_remap));
   // work units: tiles, or (split-K) tile slices, slice-major
   const int S = SPLITK ? p.sk_slices : 1;
-  const int units = p.num_tiles * S;
+  const int units = p.num_tiles * S * (SPLITK ? 1 : p.batch);
   if (wg >= units) return;
   const int my_tiles = __builtin_amdgcn_readfirstlane((units - wg + G - 1) / G);
   const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
@@ -106,7 +106,8 @@ gemm_nt_slab(GemmParams p) {
     int alt;
     int kbeg;  // first super-step of a split-K slice (0 otherwise)
   };
-  // output tile, split-K slice, and first and count of super-steps of unit u
+  // output tile, split-K slice or batch entry, and first and count of
+  // super-steps of unit u
   auto unit_of = [&](int u, int* tile, int* slice, int* kbeg, int* nks) __attribute__((always_inline)) {
     *tile = u;
     *slice = 0;
@@ -117,6 +118,11 @@ gemm_nt_slab(GemmParams p) {
       *tile = u - *slice * p.num_tiles;
       *kbeg = __builtin_amdgcn_readfirstlane(*slice * KS / S);
       *nks = __builtin_amdgcn_readfirstlane((*slice + 1) * KS / S) - *kbeg;
+    } else {
+      if (p.batch > 1) {  // slice = batch entry
+        *slice = __builtin_amdgcn_readfirstlane(u / p.num_tiles);
+        *tile = u - *slice * p.num_tiles;
+      }
     }
   };
   auto tile_desc = [&](int tile_i) __attribute__((always_inline)) {
@@ -131,11 +137,14 @@ gemm_nt_slab(GemmParams p) {
     const int n0 = tn * OUT_BN;
     const int nrows = (N - n0) < OUT_BN ? (N - n0) : OUT_BN;
     TileDesc d;
-    d.a_base = reinterpret_cast<uint64_t>(p.A + (int64_t)m0 * ld);
+    // batch entry (never with split-K): operand bases move by the strides
+    const int64_t ea = SPLITK ? 0 : (int64_t)slice * p.stride_a;
+    const int64_t eb = SPLITK ? 0 : (int64_t)slice * p.stride_b;
+    d.a_base = reinterpret_cast<uint64_t>(p.A + ea + (int64_t)m0 * ld);
     d.a_rec = (uint32_t)mrows * row_bytes;
     d.b_rec = (uint32_t)nrows * row_bytes;
-    d.b0_base = reinterpret_cast<uint64_t>(p.B + (int64_t)n0 * ld);
-    d.b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + (int64_t)n0 * ld) : d.b0_base;
+    d.b0_base = reinterpret_cast<uint64_t>(p.B + eb + (int64_t)n0 * ld);
+    d.b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + eb + (int64_t)n0 * ld) : d.b0_base;
     d.alt = SPLITK ? 0 : (p.k_alt && (tile_i & 1));
     d.kbeg = kbeg;
     return d;
@@ -334,6 +343,7 @@ gemm_nt_slab(GemmParams p) {
   const bool act_on = FFN ? (p.epi == EPI_SWIGLU) : (p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU);
   const bool bias_vec = (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
   constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
+  void* obase = p.out;  // output of the current batch entry
   auto epilogue = [&](int m0, int n0, auto f32, auto act, auto checked) __attribute__((always_inline)) {
     const int m_base = m0 + wrow_a + lx;
     int ncol[PAIRS];
@@ -380,7 +390,7 @@ gemm_nt_slab(GemmParams p) {
         if (checked && m >= M) continue;
         const bool vec = !checked || (p.out_vec && n + 8 <= N);
         if (f32) {
-          float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * N + n;
+          float* o = reinterpret_cast<float*>(obase) + (int64_t)m * N + n;
           if (vec) {
             reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
             reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
@@ -390,7 +400,7 @@ gemm_nt_slab(GemmParams p) {
               if (n + j < N) o[j] = v[j];
           }
         } else {
-          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m * N + n;
+          uint16_t* o = reinterpret_cast<uint16_t*>(obase) + (int64_t)m * N + n;
           if (vec) {
             u32x4 w;
             w[0] = pack_bf16x2(v[0], v[1]);
@@ -529,6 +539,7 @@ gemm_nt_slab(GemmParams p) {
     int tm, tn;
     tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * OUT_BN;
+    obase = static_cast<char*>(p.out) + (int64_t)h_slice * p.stride_out * (p.out_f32 ? 4 : 2);
     using T = std::true_type;
     using F = std::false_type;
     if (p.out_vec && m0 + BM <= M && n0 + OUT_BN <= N) {

@@ -270,6 +270,8 @@ struct Request {
   bool ffn;
   void* ws = nullptr;     // caller's workspace (split-K), may be null
   int64_t ws_bytes = 0;
+  int64_t batch = 1;      // batched form: entries and their element strides
+  int64_t stride_a = 0, stride_b = 0, stride_out = 0;
 };
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -282,6 +284,9 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 mm_status validate(const Request& r) {
   if (r.M < 0 || r.N < 0 || r.K < 0) return fail(MM_ERR_INVALID_VALUE, "negative size");
+  if (r.batch < 1) return fail(MM_ERR_INVALID_VALUE, "batch must be >= 1");
+  if (r.stride_a < 0 || r.stride_b < 0 || r.stride_out < 0)
+    return fail(MM_ERR_INVALID_VALUE, "negative batch stride");
   if (r.M >= (int64_t(1) << 31) || r.N >= (int64_t(1) << 31) || r.K >= (int64_t(1) << 31))
     return fail(MM_ERR_UNSUPPORTED, "M, N and K must be below 2^31");
   if (r.layout < MM_NN || r.layout > MM_TT) return fail(MM_ERR_INVALID_VALUE, "bad layout");
@@ -295,6 +300,12 @@ mm_status validate(const Request& r) {
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
   if (!aligned(r.A, 16) || !aligned(r.B, 16) || (r.ffn && !aligned(r.B2, 16)))
     return fail(MM_ERR_MISALIGNED, "operand pointers must be 16-byte aligned");
+  if (r.batch > 1) {
+    if (r.stride_a % 8 != 0 || r.stride_b % 8 != 0)
+      return fail(MM_ERR_MISALIGNED, "operand batch strides must be multiples of 8 elements");
+    if (r.stride_out < r.M * r.N)
+      return fail(MM_ERR_INVALID_VALUE, "output batch stride smaller than M * N: entries would overlap");
+  }
   if ((a_kc ? r.K : r.M) % 8 != 0)
     return fail(MM_ERR_MISALIGNED, "the contiguous extent of A must be a multiple of 8 elements");
   if ((b_kc ? r.K : r.N) % 8 != 0)
@@ -302,14 +313,17 @@ mm_status validate(const Request& r) {
   if (need_bias && !aligned(r.bias, 2)) return fail(MM_ERR_MISALIGNED, "bias must be 2-byte aligned");
   const int esize = r.out_f32 ? 4 : 2;
   if (!aligned(r.out, esize)) return fail(MM_ERR_MISALIGNED, "out must be aligned to its element size");
-  const int64_t ob = r.M * r.N * esize;
-  if (overlaps(r.out, ob, r.A, r.M * r.K * 2) || overlaps(r.out, ob, r.B, r.K * r.N * 2) ||
-      (r.ffn && overlaps(r.out, ob, r.B2, r.K * r.N * 2)) ||
+  // byte extents over every batch entry
+  const int64_t nb = r.batch - 1;
+  const int64_t ob = (nb * r.stride_out + r.M * r.N) * esize;
+  const int64_t ab = (nb * r.stride_a + r.M * r.K) * 2, bb = (nb * r.stride_b + r.K * r.N) * 2;
+  if (overlaps(r.out, ob, r.A, ab) || overlaps(r.out, ob, r.B, bb) ||
+      (r.ffn && overlaps(r.out, ob, r.B2, bb)) ||
       (need_bias && overlaps(r.out, ob, r.bias, r.N * 2)))
     return fail(MM_ERR_INVALID_VALUE, "out overlaps an input");
   if (r.ws_bytes < 0) return fail(MM_ERR_INVALID_VALUE, "negative workspace size");
-  if (r.ws && (overlaps(r.ws, r.ws_bytes, r.out, ob) || overlaps(r.ws, r.ws_bytes, r.A, r.M * r.K * 2) ||
-               overlaps(r.ws, r.ws_bytes, r.B, r.K * r.N * 2) ||
+  if (r.ws && (overlaps(r.ws, r.ws_bytes, r.out, ob) || overlaps(r.ws, r.ws_bytes, r.A, ab) ||
+               overlaps(r.ws, r.ws_bytes, r.B, bb) ||
                (need_bias && overlaps(r.ws, r.ws_bytes, r.bias, r.N * 2))))
     return fail(MM_ERR_INVALID_VALUE, "workspace overlaps an operand or the output");
   return MM_OK;
@@ -336,7 +350,7 @@ constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
 // plain K-contiguous products (no bias or activation: the slices' sums meet
 // before any epilogue math would apply)
 bool splitk_shape(const Request& r) {
-  return !r.ffn && r.epi == mmk::EPI_NONE && r.layout == MM_NT && r.K % mmk::kSlabK == 0 &&
+  return r.batch == 1 && !r.ffn && r.epi == mmk::EPI_NONE && r.layout == MM_NT && r.K % mmk::kSlabK == 0 &&
          r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31);
 }
 
@@ -390,6 +404,8 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k && S <= 1; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
+    // the batched form runs on the slab and basic kernels
+    if (r.batch > 1 && (fam == 1 || fam == 2)) continue;
     // the slab kernel runs whole super-steps of 64 k, two of them in flight
     if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
     k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam);
@@ -411,9 +427,14 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   p.epi = r.epi;
   p.out_f32 = r.out_f32 ? 1 : 0;
   const int esize = r.out_f32 ? 4 : 2;
-  p.out_vec = (aligned(r.out, 16) && (r.N * esize) % 16 == 0) ? 1 : 0;
+  p.out_vec = (aligned(r.out, 16) && (r.N * esize) % 16 == 0 &&
+               (r.batch == 1 || (r.stride_out * esize) % 16 == 0)) ? 1 : 0;
   const int64_t tm = cdiv(r.M, c.bm), tn = cdiv(r.N, out_bn);
-  if (tm * tn >= (int64_t(1) << 31)) return fail(MM_ERR_UNSUPPORTED, "too many tiles");
+  if (tm * tn * r.batch >= (int64_t(1) << 31)) return fail(MM_ERR_UNSUPPORTED, "too many tiles");
+  p.batch = (int)r.batch;
+  p.stride_a = r.stride_a;
+  p.stride_b = r.stride_b;
+  p.stride_out = r.stride_out;
   p.tiles_m = (int)tm;
   p.tiles_n = (int)tn;
   p.num_tiles = (int)(tm * tn);
@@ -467,7 +488,7 @@ mm_status run(const Request& r, void* stream) {
     }
   }
   if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
-  const int64_t units = (int64_t)pl.p.num_tiles * pl.p.sk_slices;
+  const int64_t units = (int64_t)pl.p.num_tiles * pl.p.sk_slices * pl.p.batch;
   int64_t grid = c.grid > 0 ? c.grid : (int64_t)cus * occ;
   if (pl.p.sk_slices > 1 && grid > (int64_t)cus * occ) grid = (int64_t)cus * occ;
   if (grid > units) grid = units;
@@ -513,6 +534,36 @@ mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, i
   const int e = map_epilogue(epi);
   if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
   Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  return run(r, stream);
+}
+
+mm_status mm_matmul_batched(const void* A, const void* B, void* out, int64_t batch, int64_t M,
+                            int64_t N, int64_t K, int64_t stride_a, int64_t stride_b,
+                            int64_t stride_out, mm_layout layout, mm_out_dtype out_dtype,
+                            void* stream) {
+  g_last_error.clear();
+  if (out_dtype != MM_OUT_BF16 && out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_INVALID_VALUE, "bad output dtype");
+  Request r{A, B, nullptr, nullptr, out, M, N, K, (int)layout, mmk::EPI_NONE,
+            out_dtype == MM_OUT_F32, false};
+  r.batch = batch;
+  r.stride_a = stride_a;
+  r.stride_b = stride_b;
+  r.stride_out = stride_out;
+  return run(r, stream);
+}
+
+mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void* out, int64_t batch,
+                            int64_t M, int64_t N, int64_t K, int64_t stride_x, int64_t stride_w,
+                            int64_t stride_out, mm_layout layout, mm_epilogue epi, void* stream) {
+  g_last_error.clear();
+  const int e = map_epilogue(epi);
+  if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
+  Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  r.batch = batch;
+  r.stride_a = stride_x;
+  r.stride_b = stride_w;
+  r.stride_out = stride_out;
   return run(r, stream);
 }
 

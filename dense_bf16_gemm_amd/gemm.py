@@ -165,3 +165,88 @@ def ffn_swiglu(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor,
                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Llama FFN gate/up: SiLU(x @ W_gate.T) * (x @ W_up.T) in one kernel."""
     return ffn_glu(x, W_gate, W_up, "silu", out)
+
+
+def _batched(t: torch.Tensor, name: str):
+    """(entry layout letter, batch size, batch stride in elements) of a 3-D
+    operand whose entries are contiguous or transposed-contiguous matrices;
+    a batch dimension of size 1 or stride 0 broadcasts."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D [batch, rows, cols], got shape {tuple(t.shape)}")
+    if t.shape[0] == 0:
+        raise ValueError(f"{name} has an empty batch dimension")
+    letter = _letter(t[0], name)
+    stride = t.stride(0) if t.shape[0] > 1 else 0
+    return letter, t.shape[0], stride
+
+
+def _batch_count(*sizes: int) -> int:
+    b = max(sizes)
+    for s in sizes:
+        if s not in (1, b):
+            raise ValueError(f"batch sizes {sizes} do not broadcast")
+    return b
+
+
+def bmm(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Batched MatmulOp: out[b] = A[b] @ B[b] for A [batch, M, K], B [batch, K, N]
+    (entries contiguous or transposed views; a batch dimension of 1, or an
+    expanded one with stride 0, is broadcast).  One kernel for all entries."""
+    _check(A, "A")
+    _check(B, "B")
+    la, ba, sa = _batched(A, "A")
+    lb, bb, sb = _batched(B, "B")
+    _, M, K = A.shape
+    _, K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    batch = _batch_count(ba, bb)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=out_dtype, device=A.device)
+    elif out.shape != (batch, M, N) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [batch, M, N] tensor of out_dtype")
+    lib = binding.load()
+    st = lib.mm_matmul_batched(A.data_ptr(), B.data_ptr(), out.data_ptr(), batch, M, N, K, sa, sb,
+                               M * N, binding.LAYOUTS[la + lb],
+                               binding.OUT_DTYPES["f32" if out_dtype == torch.float32 else "bf16"],
+                               _stream())
+    binding.check(st, "mm_matmul_batched")
+    return out
+
+
+def linear_batched(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                   epilogue: str = "none", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Batched LinearOp: out[b] = epi(x[b] @ W[b].T + bias) for x [batch, M, K] and
+    W [batch, N, K] or [N, K] (one weight for every entry); bias [N] shared."""
+    _check(x, "x")
+    _check(W, "W")
+    if W.dim() == 2:
+        W = W.unsqueeze(0)
+    lx, bx, sx = _batched(x, "x")
+    lw, bw, sw = _batched(W.transpose(1, 2), "W.T")
+    _, M, K = x.shape
+    _, N, K2 = W.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if epilogue not in binding.EPILOGUES:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    if epilogue in ("bias", "bias_gelu_tanh"):
+        if bias is None:
+            raise ValueError(f"epilogue {epilogue!r} needs a bias")
+        _check(bias, "bias")
+        if bias.shape != (N,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous [N] tensor")
+    batch = _batch_count(bx, bw)
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (batch, M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [batch, M, N] tensor")
+    lib = binding.load()
+    st = lib.mm_linear_batched(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
+                               out.data_ptr(), batch, M, N, K, sx, sw, M * N,
+                               binding.LAYOUTS[lx + lw], binding.EPILOGUES[epilogue], _stream())
+    binding.check(st, "mm_linear_batched")
+    return out

@@ -104,6 +104,30 @@ mm_status mm_matmul(const void* A, const void* B, void* out, int64_t M, int64_t 
 mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, int64_t M,
                     int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* stream);
 
+/* Batched forms (the pages' BMNK operands: PR "Implement persistent matmul
+ * scheduling", description -- inputs canonicalized to batch, M, N, K
+ * dimensions, broadcast inputs through fusedMultiplySum):
+ *   out[b] = op(A[b]) . op(B[b])          (mm_matmul_batched)
+ *   out[b] = epi(op(x[b]) . op(W[b]) + bias)   (mm_linear_batched)
+ * for b < batch, in one kernel.  Entry b of an operand starts stride_*
+ * elements after entry 0; a stride of 0 broadcasts that operand to every
+ * entry (e.g. one weight for all batch entries).  Each entry is laid out as
+ * the unbatched call's operand (`layout` as for mm_matmul / mm_linear).
+ * bias [N] is shared by all entries.
+ *   stride_a / stride_x, stride_b / stride_w   >= 0, multiples of 8 when
+ *                              batch > 1 (entries stay 16-byte aligned)
+ *   stride_out   >= M * N when batch > 1 (entries must not overlap)
+ * With batch == 1 the strides are ignored and the calls equal the unbatched
+ * ones.  Errors as for mm_matmul, plus MM_ERR_INVALID_VALUE for batch < 1,
+ * negative strides, or output entries that would overlap.                  */
+mm_status mm_matmul_batched(const void* A, const void* B, void* out, int64_t batch, int64_t M,
+                            int64_t N, int64_t K, int64_t stride_a, int64_t stride_b,
+                            int64_t stride_out, mm_layout layout, mm_out_dtype out_dtype,
+                            void* stream);
+mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void* out, int64_t batch,
+                            int64_t M, int64_t N, int64_t K, int64_t stride_x, int64_t stride_w,
+                            int64_t stride_out, mm_layout layout, mm_epilogue epi, void* stream);
+
 /* Split-K workspace (PR "Implement persistent matmul scheduling", review
  * notes: splitting the K loop over workgroups, split-K and stream-K, named
  * there and left out of the persistent scheduler).  When a plain K-contiguous

@@ -167,3 +167,20 @@ def test_schedule_xcd_locality():
         cols = {tn for _, tn in tiles}
         # 32 workgroups of an XCD cover an 8-row x 4-column block of tiles
         assert len(rows) == 8 and len(cols) == 4, (x, rows, cols)
+
+
+def test_batched_argument_checks():
+    """Checked before any HIP call: batch < 1, negative or misaligned strides,
+    overlapping output entries."""
+    lib = binding.load()
+    A, B, out = 4096, 8192, 1 << 30  # fake, 16-byte aligned, disjoint device addresses
+    M, N, K = 64, 64, 64
+    cases = [
+        (0, 0, 0, M * N, binding.MM_ERR_INVALID_VALUE),          # batch 0
+        (2, -8, 0, M * N, binding.MM_ERR_INVALID_VALUE),         # negative stride
+        (2, 12, 0, M * N, binding.MM_ERR_MISALIGNED),            # stride not a multiple of 8
+        (2, M * K, K * N, M * N - 1, binding.MM_ERR_INVALID_VALUE),  # output entries overlap
+    ]
+    for batch, sa, sb, so, want in cases:
+        st = lib.mm_matmul_batched(A, B, out, batch, M, N, K, sa, sb, so, binding.LAYOUTS["nt"], 0, None)
+        assert st == want, (batch, sa, sb, so, st)

@@ -163,6 +163,80 @@ def test_mapping_bitexact_matmul_f32(dev, cfg, layout):
         np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
+# ------------------------------------------------------------ batched forms
+def call_matmul_batched(A, B, batch, M, N, K, sa, sb, so, layout, out_f32, out):
+    lib = binding.load()
+    st = lib.mm_matmul_batched(A.data_ptr(), B.data_ptr(), out.data_ptr(), batch, M, N, K, sa, sb, so,
+                               binding.LAYOUTS[layout], 1 if out_f32 else 0, stream())
+    binding.check(st, "mm_matmul_batched")
+
+
+# (batch, M, N, K, layout, B broadcast): K multiples of 64 with NT take the
+# slab kernel, the rest the basic kernel (the batched form runs on those two)
+BATCH_CASES = [
+    (3, 129, 136, 200, "nt", False),
+    (2, 300, 264, 192, "nt", False),
+    (3, 257, 520, 128, "nt", True),
+    (4, 64, 72, 128, "nn", False),
+    (2, 136, 200, 72, "tn", True),
+    (2, 136, 208, 64, "tt", False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BATCH_CASES)))
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_batched_mapping_bitexact(dev, case, out_f32):
+    batch, M, N, K, layout, bcast = BATCH_CASES[case]
+    say("batched mapping", BATCH_CASES[case], "f32" if out_f32 else "bf16")
+    As, Bs = [], []
+    for b in range(batch):
+        A, B = synth.dense_int_operands(M, N, K, layout, seed=100 * b + M + N + K)
+        As.append(A)
+        Bs.append(Bs[0] if (bcast and b) else B)
+    A_all = torch.stack(As).to(dev)
+    B_all = (Bs[0].unsqueeze(0) if bcast else torch.stack(Bs)).to(dev)
+    sa = As[0].numel()
+    sb = 0 if bcast else Bs[0].numel()
+    out = torch.full((batch, M, N), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                     device=dev)
+    call_matmul_batched(A_all, B_all, batch, M, N, K, sa, sb, M * N, layout, out_f32, out)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref, bits = oracle.gemm(synth.bits(As[b]), synth.bits(Bs[b]), layout)
+        if out_f32:
+            np.testing.assert_array_equal(out[b].cpu().numpy(), ref)
+        else:
+            np.testing.assert_array_equal(to_bits(out[b]), bits)
+
+
+def test_batched_torch_views_and_linear(dev):
+    """mm.bmm on torch views (a transposed batch, a broadcast entry) and the
+    batched linear layer with a shared weight and bias + GELU."""
+    batch, M, N, K = 3, 200, 264, 256
+    say("batched views + linear", (batch, M, N, K))
+    A = synth.randn_bf16((batch, M, K), 1.0, 21).to(dev)
+    Bt = synth.randn_bf16((batch, N, K), K ** -0.5, 22).to(dev)
+    got = mm.bmm(A, Bt.transpose(1, 2), torch.float32)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        y, _ = oracle.gemm(synth.bits(A[b].cpu()), synth.bits(Bt[b].cpu()), "nt")
+        assert tol_excess(got[b].cpu().numpy(), y, 1e-3) <= 0
+    W = synth.randn_bf16((N, K), K ** -0.5, 23).to(dev)
+    bias = synth.randn_bf16((N,), 1.0, 24).to(dev)
+    got = mm.linear_batched(A, W, bias, "bias_gelu_tanh")
+    torch.cuda.synchronize()
+    for b in range(batch):
+        y, _ = oracle.gemm(synth.bits(A[b].cpu()), synth.bits(W.cpu()), "nt", "bias_gelu_tanh",
+                           bias=synth.bits(bias.cpu()))
+        assert tol_excess(got[b].float().cpu().numpy(), y, 2e-2) <= 0
+    # a broadcast activation entry (expand gives stride 0) against per-entry weights
+    got = mm.bmm(A[:1].expand(batch, M, K), Bt.transpose(1, 2), torch.float32)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        y, _ = oracle.gemm(synth.bits(A[0].cpu()), synth.bits(Bt[b].cpu()), "nt")
+        assert tol_excess(got[b].cpu().numpy(), y, 1e-3) <= 0
+
+
 # ------------------------------------------------------------ split-K
 # (M, N, K, configuration): few 256 x 256 output tiles, long K.  The forced
 # slice counts with small grids make slices wait on other workgroups across
