@@ -45,6 +45,52 @@ __device__ __forceinline__ float gelu_tanh_fast(float t) {
   return t * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// The same GELU on eight independent values, one operation across all eight
+// at a time, so that the exp2 and reciprocal latencies overlap.
+__device__ __forceinline__ void gelu_tanh8(float (&v)[8]) {
+  constexpr float c1 = -2.3022081983f;
+  constexpr float c2 = -0.1029432396f;
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = v[j] * v[j];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = __builtin_fmaf(c2, e[j], c1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = v[j] * e[j];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(e[j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = 1.0f + e[j];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_rcpf(e[j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = v[j] * e[j];
+}
+
+// The scalar bookkeeping at the head of a k-step (ring units, descriptor
+// bases, LDS destinations) is a dependent chain; left in front of the first
+// MFMA it idles the matrix core, since one wave issues at most one
+// instruction per four cycles.  These scheduling groups spread it over the
+// issue slots between the k-step's first four MFMAs: N scalar instructions
+// after each of the first three, LAST after the fourth.
+template <int N, int LAST>
+__device__ __forceinline__ void interleave_scalar() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);  // scalar ALU
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, LAST, 0);
+}
+
 // SiLU as g / (1 + 2^(-g log2 e)).
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
@@ -292,6 +338,7 @@ gemm_nt_slab(GemmParams p) {
         read_b(1, 2 * r, 1, b_cur);
         read_b(1, 2 * r + 1, 1, b_cur);
       }
+      if (r == 0) interleave_scalar<6, 8>();
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(r, 0, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -323,6 +370,7 @@ gemm_nt_slab(GemmParams p) {
         read_b(0, 2 * (p - 1), 0, b_nxt);
         read_b(0, 2 * (p - 1) + 1, 0, b_nxt);
       }
+      if (p == 1) interleave_scalar<3, 3>();
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(r, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -376,16 +424,17 @@ gemm_nt_slab(GemmParams p) {
       for (int pr = 0; pr < PAIRS; ++pr) {
         const int n = ncol[pr];
         float v[8];
+        if constexpr (FFN) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float a = acc[fm][2 * pr + (j >> 2)][j & 3];
-          if constexpr (FFN) {
+          for (int j = 0; j < 8; ++j) {
+            const float a = acc[fm][2 * pr + (j >> 2)][j & 3];
             const float u = acc[fm][FN / 2 + 2 * pr + (j >> 2)][j & 3];
             v[j] = (act ? silu_fast(a) : a) * u;
-          } else {
-            const float t = a + bv[pr][j];
-            v[j] = act ? gelu_tanh_fast(t) : t;
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = acc[fm][2 * pr + (j >> 2)][j & 3] + bv[pr][j];
+          if (act) gelu_tanh8(v);
         }
         if (checked && m >= M) continue;
         const bool vec = !checked || (p.out_vec && n + 8 <= N);
