@@ -74,21 +74,42 @@ __device__ __forceinline__ void gelu_tanh8(float (&v)[8]) {
 }
 
 // The scalar bookkeeping at the head of a k-step (ring units, descriptor
-// bases, LDS destinations) is a dependent chain; left in front of the first
-// MFMA it idles the matrix core, since one wave issues at most one
-// instruction per four cycles.  These scheduling groups spread it over the
-// issue slots between the k-step's first four MFMAs: N scalar instructions
-// after each of the first three, LAST after the fourth.
-template <int N, int LAST>
-__device__ __forceinline__ void interleave_scalar() {
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);  // scalar ALU
+// bases, LDS destinations: a dependent chain of ~25 instructions) would idle
+// the matrix core if it ran in front of the first MFMA, since one wave issues
+// at most one instruction per four cycles and an MFMA takes sixteen.  These
+// scheduling groups spread it, with the row's copy and fragment reads, over
+// the three free issue slots after each of the row's eight MFMAs.
+// 0x008: MFMA, 0x006: scalar or vector ALU, 0x020: memory read (the copy),
+// 0x100: LDS read.
+__device__ __forceinline__ void spread_first_row_a() {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+}
+__device__ __forceinline__ void spread_first_row_b() {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x004, N, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x004, LAST, 0);
+  __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
 }
 
 // SiLU as g / (1 + 2^(-g log2 e)).
@@ -338,9 +359,13 @@ gemm_nt_slab(GemmParams p) {
         read_b(1, 2 * r, 1, b_cur);
         read_b(1, 2 * r + 1, 1, b_cur);
       }
-      if (r == 0) interleave_scalar<6, 8>();
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_half(r, 0, 1);
+      if (r == 0) {
+        mfma_half(r, 0, 1);
+        spread_first_row_a();
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(r, 0, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       read_a(r, 1, a_cur);
       __builtin_amdgcn_sched_barrier(0);
@@ -370,9 +395,13 @@ gemm_nt_slab(GemmParams p) {
         read_b(0, 2 * (p - 1), 0, b_nxt);
         read_b(0, 2 * (p - 1) + 1, 0, b_nxt);
       }
-      if (p == 1) interleave_scalar<3, 3>();
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_half(r, 1, 1);
+      if (p == 1) {
+        mfma_half(r, 1, 1);
+        spread_first_row_b();
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half(r, 1, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       read_a(r, 0, a_nxt);
       __builtin_amdgcn_sched_barrier(0);
@@ -396,6 +425,25 @@ gemm_nt_slab(GemmParams p) {
     const int m_base = m0 + wrow_a + lx;
     int ncol[PAIRS];
     float bv[PAIRS][8];
+    // A tile whose columns all lie inside N with a 16-byte aligned bias (the
+    // same for the whole wave) loads all of its bias vectors before the first
+    // wait; other tiles check each lane's columns.
+    const bool bias_fast = !FFN && has_bias && bias_vec && n0 + OUT_BN <= N;
+    if (bias_fast) {
+      u32x4 w[PAIRS];
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        ncol[pr] = n0 + wrow_b + 32 * pr + 8 * lk;
+        w[pr] = *reinterpret_cast<const u32x4*>(p.bias + ncol[pr]);
+      }
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bv[pr][2 * j] = __builtin_bit_cast(float, w[pr][j] << 16);
+          bv[pr][2 * j + 1] = __builtin_bit_cast(float, w[pr][j] & 0xffff0000u);
+        }
+    } else
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
       const int n = FFN ? n0 + wave_n * (WTN / 2) + 32 * pr + 8 * lk : n0 + wrow_b + 32 * pr + 8 * lk;
