@@ -237,10 +237,13 @@ gemm_nt_slab(GemmParams p) {
     const int r0 = 8 * (c * NW + wave);
     *up = false;
     if constexpr (FFN) {
-      // each wave column's WTN weight rows: WTN/2 gate rows, then the up rows
-      const int wb = r0 / WTN, within = r0 % WTN;
-      *up = within >= WTN / 2;
-      return wb * (WTN / 2) + (*up ? within - WTN / 2 : within);
+      // each wave column's WTN weight rows: WTN/2 gate rows, then the up rows.
+      // The NW waves' rows of copy c lie in one half of a wave column, so
+      // the half (and with it the operand) follows from c alone.
+      static_assert((WTN / 2) % (8 * NW) == 0, "a copy's rows stay in one half");
+      const int c0 = 8 * c * NW;  // first row of copy c over all waves
+      *up = (c0 % WTN) >= WTN / 2;
+      return (c0 / WTN) * (WTN / 2) + (c0 % WTN) - (*up ? WTN / 2 : 0) + 8 * wave;
     }
     return r0;
   };
