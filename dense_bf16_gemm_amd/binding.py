@@ -24,6 +24,7 @@ EXPORTS = (
     "mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
     "mm_describe_config", "mm_debug_schedule", "mm_status_string", "mm_last_error",
     "mm_workspace_size", "mm_matmul_ws", "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched",
+    "mm_linear_preact",
 )
 
 _lib = None
@@ -55,13 +56,14 @@ def load(path: str = LIB_PATH):
     lib.mm_linear_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp, i64, vp]
     lib.mm_matmul_batched.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
     lib.mm_linear_batched.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    lib.mm_linear_preact.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.mm_set_config.argtypes = [ctypes.c_char_p]
     lib.mm_describe_config.argtypes = [ci, i64, i64, i64, ci, ctypes.c_char_p, i64]
     lib.mm_debug_schedule.argtypes = [ci, i64, i64, i64, ci, i64, ctypes.POINTER(ctypes.c_int32), i64,
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
                  "mm_describe_config", "mm_debug_schedule", "mm_workspace_size", "mm_matmul_ws",
-                 "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched"):
+                 "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched", "mm_linear_preact"):
         getattr(lib, name).restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p

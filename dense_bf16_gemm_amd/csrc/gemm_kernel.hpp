@@ -69,6 +69,8 @@ struct GemmParams {
   const uint16_t* B2;    // FFN up weight [N][K], else unused
   const uint16_t* bias;  // [N] or null
   void* out;             // [M][N] bf16 or fp32
+  void* out_pre;         // null, or a second [M][N] output of the same type that
+                         // receives the pre-activation of a GELU epilogue
   int M, N, K;
   int epi;
   int out_f32;
@@ -174,6 +176,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Eight consecutive outputs of row m from column n on, into the [M][N]
+// row-major `base` (fp32 or bf16): 16-byte stores when `vec` and the eight
+// columns lie inside N, else element by element.
+__device__ __forceinline__ void store_row8(void* base, int f32, int vec, int m, int N, int n,
+                                           const float (&v)[8]) {
+  if (f32) {
+    float* o = reinterpret_cast<float*>(base) + (int64_t)m * N + n;
+    if (vec && n + 8 <= N) {
+      reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
+      reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < N) o[j] = v[j];
+    }
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(base) + (int64_t)m * N + n;
+    if (vec && n + 8 <= N) {
+      u32x4 w;
+      w[0] = pack_bf16x2(v[0], v[1]);
+      w[1] = pack_bf16x2(v[2], v[3]);
+      w[2] = pack_bf16x2(v[4], v[5]);
+      w[3] = pack_bf16x2(v[6], v[7]);
+      *reinterpret_cast<u32x4*>(o) = w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < N) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -451,12 +485,18 @@ gemm_persistent(GemmParams p) {
             const float u = acc[fm][FN / 2 + 2 * pr + (j >> 2)][j & 3];
             y = (p.epi == EPI_SWIGLU) ? silu(a) * u : a * u;
           } else {
-            const float t = a + bv[j];
-            y = gelu ? gelu_tanh(t) : t;
+            y = a + bv[j];  // the pre-activation, activated after its store
           }
           v[j] = y;
         }
         if (m >= M) continue;
+        if constexpr (!FFN) {
+          if (p.out_pre) store_row8(p.out_pre, p.out_f32, p.out_vec, m, N, n, v);
+          if (gelu) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = gelu_tanh(v[j]);
+          }
+        }
         if (p.out_f32) {
           float* o = reinterpret_cast<float*>(bview.out) + (int64_t)m * N + n;
           if (p.out_vec && n + 8 <= N) {

@@ -117,10 +117,14 @@ __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
 }
 
-template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false>
+template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
+  // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
+  // a separate instance because any extra epilogue path in the default one
+  // changes the register allocation of its K loop.
+  static_assert(!(PRE && (FFN || SPLITK)), "pre-activation output of the linear GELU form only");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM;
   constexpr int WTN = BN / WGN;
@@ -424,7 +428,37 @@ gemm_nt_slab(GemmParams p) {
   const bool bias_vec = (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
   constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
   void* obase = p.out;  // output of the current batch entry
-  auto epilogue = [&](int m0, int n0, auto f32, auto act, auto checked) __attribute__((always_inline)) {
+  // 8 consecutive outputs of row m from column n on: one 16-byte (bf16) or
+  // two 16-byte (fp32) stores when `vec`, else element by element up to N.
+  auto store8 = [&](void* base, int m, int n, const float (&v)[8], auto f32, bool vec)
+      __attribute__((always_inline)) {
+    if (f32) {
+      float* o = reinterpret_cast<float*>(base) + (int64_t)m * N + n;
+      if (vec) {
+        reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
+        reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (n + j < N) o[j] = v[j];
+      }
+    } else {
+      uint16_t* o = reinterpret_cast<uint16_t*>(base) + (int64_t)m * N + n;
+      if (vec) {
+        u32x4 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        w[2] = pack_bf16x2(v[4], v[5]);
+        w[3] = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<u32x4*>(o) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (n + j < N) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
+      }
+    }
+  };
+  auto epilogue = [&](int m0, int n0, auto f32, auto act, auto checked, auto pre) __attribute__((always_inline)) {
     const int m_base = m0 + wrow_a + lx;
     int ncol[PAIRS];
     float bv[PAIRS][8];
@@ -485,35 +519,15 @@ gemm_nt_slab(GemmParams p) {
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] = acc[fm][2 * pr + (j >> 2)][j & 3] + bv[pr][j];
-          if (act) gelu_tanh8(v);
         }
         if (checked && m >= M) continue;
         const bool vec = !checked || (p.out_vec && n + 8 <= N);
-        if (f32) {
-          float* o = reinterpret_cast<float*>(obase) + (int64_t)m * N + n;
-          if (vec) {
-            reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
-            reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (n + j < N) o[j] = v[j];
-          }
-        } else {
-          uint16_t* o = reinterpret_cast<uint16_t*>(obase) + (int64_t)m * N + n;
-          if (vec) {
-            u32x4 w;
-            w[0] = pack_bf16x2(v[0], v[1]);
-            w[1] = pack_bf16x2(v[2], v[3]);
-            w[2] = pack_bf16x2(v[4], v[5]);
-            w[3] = pack_bf16x2(v[6], v[7]);
-            *reinterpret_cast<u32x4*>(o) = w;
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (n + j < N) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
-          }
+        if constexpr (!FFN) {
+          // second output: the pre-activation (bias added, before GELU)
+          if (pre) store8(p.out_pre, m, n, v, f32, vec);
+          if (act) gelu_tanh8(v);
         }
+        store8(obase, m, n, v, f32, vec);
       }
     }
   };
@@ -642,16 +656,19 @@ gemm_nt_slab(GemmParams p) {
     obase = static_cast<char*>(p.out) + (int64_t)h_slice * p.stride_out * (p.out_f32 ? 4 : 2);
     using T = std::true_type;
     using F = std::false_type;
-    if (p.out_vec && m0 + BM <= M && n0 + OUT_BN <= N) {
+    if constexpr (PRE) {  // bf16, GELU: unmasked on interior tiles
+      if (p.out_vec && m0 + BM <= M && n0 + OUT_BN <= N) epilogue(m0, n0, F{}, T{}, F{}, T{});
+      else epilogue(m0, n0, F{}, T{}, T{}, T{});
+    } else if (p.out_vec && m0 + BM <= M && n0 + OUT_BN <= N) {
       if (FFN || !p.out_f32) {
-        if (act_on) epilogue(m0, n0, F{}, T{}, F{});
-        else epilogue(m0, n0, F{}, F{}, F{});
+        if (act_on) epilogue(m0, n0, F{}, T{}, F{}, F{});
+        else epilogue(m0, n0, F{}, F{}, F{}, F{});
       } else {
-        if (act_on) epilogue(m0, n0, T{}, T{}, F{});
-        else epilogue(m0, n0, T{}, F{}, F{});
+        if (act_on) epilogue(m0, n0, T{}, T{}, F{}, F{});
+        else epilogue(m0, n0, T{}, F{}, F{}, F{});
       }
     } else {
-      epilogue(m0, n0, p.out_f32 != 0, act_on, T{});
+      epilogue(m0, n0, p.out_f32 != 0, act_on, T{}, F{});
     }
   }
 }

@@ -44,6 +44,7 @@ struct KernelEntry {
   const void* fn;
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
   bool splitk = false;         // gemm_nt_slab<..., SPLITK>: needs a workspace
+  bool pre = false;            // gemm_nt_slab<..., PRE>: stores the pre-activation too
 };
 
 #define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
@@ -66,12 +67,18 @@ struct KernelEntry {
   {256, 256, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true>), {0}, true}
 
+#define MM_KSP()                                                                           \
+  {256, 256, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, true>), {0}, \
+   false, true}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
     MM_KSK(),
+    MM_KSP(),
     MM_KS(false),
     MM_KS(true),
     MM_KPP(false),
@@ -95,10 +102,10 @@ KernelEntry g_kernels[] = {
 constexpr int kNumKernels = sizeof(g_kernels) / sizeof(g_kernels[0]);
 
 KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe,
-                         bool splitk = false) {
+                         bool splitk = false, bool pre = false) {
   for (auto& k : g_kernels)
     if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
-        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk)
+        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk && k.pre == pre)
       return &k;
   return nullptr;
 }
@@ -272,6 +279,7 @@ struct Request {
   int64_t ws_bytes = 0;
   int64_t batch = 1;      // batched form: entries and their element strides
   int64_t stride_a = 0, stride_b = 0, stride_out = 0;
+  void* out_pre = nullptr;  // second output: the pre-activation (GELU epilogues)
 };
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -321,6 +329,15 @@ mm_status validate(const Request& r) {
       (r.ffn && overlaps(r.out, ob, r.B2, bb)) ||
       (need_bias && overlaps(r.out, ob, r.bias, r.N * 2)))
     return fail(MM_ERR_INVALID_VALUE, "out overlaps an input");
+  if (r.out_pre) {
+    if (r.ffn || r.batch != 1 || (r.epi != mmk::EPI_GELU && r.epi != mmk::EPI_BIAS_GELU))
+      return fail(MM_ERR_INVALID_VALUE, "a pre-activation output needs an unbatched linear GELU epilogue");
+    if (!aligned(r.out_pre, esize))
+      return fail(MM_ERR_MISALIGNED, "preact must be aligned to its element size");
+    if (overlaps(r.out_pre, ob, r.A, ab) || overlaps(r.out_pre, ob, r.B, bb) ||
+        overlaps(r.out_pre, ob, r.out, ob) || (need_bias && overlaps(r.out_pre, ob, r.bias, r.N * 2)))
+      return fail(MM_ERR_INVALID_VALUE, "preact overlaps an input or out");
+  }
   if (r.ws_bytes < 0) return fail(MM_ERR_INVALID_VALUE, "negative workspace size");
   if (r.ws && (overlaps(r.ws, r.ws_bytes, r.out, ob) || overlaps(r.ws, r.ws_bytes, r.A, ab) ||
                overlaps(r.ws, r.ws_bytes, r.B, bb) ||
@@ -404,11 +421,12 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k && S <= 1; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
-    // the batched form runs on the slab and basic kernels
-    if (r.batch > 1 && (fam == 1 || fam == 2)) continue;
+    // the batched form and the pre-activation output run on the slab and
+    // basic kernels
+    if ((r.batch > 1 || r.out_pre) && (fam == 1 || fam == 2)) continue;
     // the slab kernel runs whole super-steps of 64 k, two of them in flight
     if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
-    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam);
+    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile
   if (!k) k = find_kernel(c.bm, c.bn, 2, 2, a_kc, b_kc, r.ffn, 0);
@@ -421,6 +439,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   p.B2 = static_cast<const uint16_t*>(r.B2);
   p.bias = static_cast<const uint16_t*>(r.bias);
   p.out = r.out;
+  p.out_pre = r.out_pre;
   p.M = (int)r.M;
   p.N = (int)r.N;
   p.K = (int)r.K;
@@ -428,7 +447,8 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   p.out_f32 = r.out_f32 ? 1 : 0;
   const int esize = r.out_f32 ? 4 : 2;
   p.out_vec = (aligned(r.out, 16) && (r.N * esize) % 16 == 0 &&
-               (r.batch == 1 || (r.stride_out * esize) % 16 == 0)) ? 1 : 0;
+               (r.batch == 1 || (r.stride_out * esize) % 16 == 0) &&
+               (!r.out_pre || aligned(r.out_pre, 16))) ? 1 : 0;
   const int64_t tm = cdiv(r.M, c.bm), tn = cdiv(r.N, out_bn);
   if (tm * tn * r.batch >= (int64_t(1) << 31)) return fail(MM_ERR_UNSUPPORTED, "too many tiles");
   p.batch = (int)r.batch;
@@ -534,6 +554,20 @@ mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, i
   const int e = map_epilogue(epi);
   if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
   Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  return run(r, stream);
+}
+
+mm_status mm_linear_preact(const void* x, const void* W, const void* bias, void* out, void* preact,
+                           int64_t M, int64_t N, int64_t K, mm_layout layout, mm_epilogue epi,
+                           void* stream) {
+  g_last_error.clear();
+  const int e = map_epilogue(epi);
+  if (e < 0) return fail(MM_ERR_INVALID_VALUE, "bad epilogue");
+  if (!preact && M > 0 && N > 0) return fail(MM_ERR_INVALID_VALUE, "null preact pointer");
+  Request r{x, W, nullptr, bias, out, M, N, K, (int)layout, e, false, false};
+  r.out_pre = preact;
+  if (M > 0 && N > 0 && e != mmk::EPI_GELU && e != mmk::EPI_BIAS_GELU)
+    return fail(MM_ERR_INVALID_VALUE, "a pre-activation output needs a GELU epilogue");
   return run(r, stream);
 }
 

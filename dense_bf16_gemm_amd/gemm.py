@@ -136,6 +136,43 @@ def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None
     return out
 
 
+def linear_preact(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                  epilogue: str = "bias_gelu_tanh", out: Optional[torch.Tensor] = None,
+                  preact: Optional[torch.Tensor] = None):
+    """LinearOp with two outputs from one kernel: preact = x @ W.T (+ bias) and
+    out = GELU_tanh(preact), both bf16 [M, N]; epilogue gelu_tanh or
+    bias_gelu_tanh.  Returns (out, preact)."""
+    _check(x, "x")
+    _check(W, "W")
+    M, K = x.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if epilogue not in ("gelu_tanh", "bias_gelu_tanh"):
+        raise ValueError("linear_preact needs epilogue gelu_tanh or bias_gelu_tanh")
+    if epilogue == "bias_gelu_tanh":
+        if bias is None:
+            raise ValueError("epilogue 'bias_gelu_tanh' needs a bias")
+        _check(bias, "bias")
+        if bias.shape != (N,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous [N] tensor")
+    layout = _letter(x, "x") + _letter(W.t(), "W.T")
+    res = []
+    for t, nm in ((out, "out"), (preact, "preact")):
+        if t is None:
+            t = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        elif t.shape != (M, N) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous bf16 [M, N] tensor")
+        res.append(t)
+    out, preact = res
+    lib = binding.load()
+    st = lib.mm_linear_preact(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
+                              out.data_ptr(), preact.data_ptr(), M, N, K, binding.LAYOUTS[layout],
+                              binding.EPILOGUES[epilogue], _stream())
+    binding.check(st, "mm_linear_preact")
+    return out, preact
+
+
 def ffn_glu(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, act: str = "silu",
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Horizontally fused FFN: out = act(x @ W_gate.T) * (x @ W_up.T), one kernel;

@@ -104,6 +104,24 @@ mm_status mm_matmul(const void* A, const void* B, void* out, int64_t M, int64_t 
 mm_status mm_linear(const void* x, const void* W, const void* bias, void* out, int64_t M,
                     int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* stream);
 
+/* LinearOp with two epilogue outputs (issue "Automate performant Hopper
+ * matmul", section "Epilogue", TMA store: staging memory reused when a
+ * fusion has several outputs; here the pre-activation beside the activation,
+ * which a backward pass of GELU needs):
+ *   preact[M][N] = op(x) . op(W) + bias          (the bias term for
+ *                                                 MM_EPI_BIAS_GELU_TANH only)
+ *   out[M][N]    = GELU_tanh(preact), computed from the fp32 value before
+ *                  preact is rounded
+ * both bf16 (RNE), written by the same kernel from the same accumulators.
+ *   epi     MM_EPI_GELU_TANH or MM_EPI_BIAS_GELU_TANH; any other returns
+ *           MM_ERR_INVALID_VALUE
+ *   preact  caller-owned device memory, element aligned, not overlapping x, W,
+ *           bias or out (else MM_ERR_INVALID_VALUE / MM_ERR_MISALIGNED)
+ * Other arguments, alignment rules and errors as for mm_linear.              */
+mm_status mm_linear_preact(const void* x, const void* W, const void* bias, void* out, void* preact,
+                           int64_t M, int64_t N, int64_t K, mm_layout layout, mm_epilogue epi,
+                           void* stream);
+
 /* Batched forms (the pages' BMNK operands: PR "Implement persistent matmul
  * scheduling", description -- inputs canonicalized to batch, M, N, K
  * dimensions, broadcast inputs through fusedMultiplySum):

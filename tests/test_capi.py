@@ -184,3 +184,26 @@ def test_batched_argument_checks():
     for batch, sa, sb, so, want in cases:
         st = lib.mm_matmul_batched(A, B, out, batch, M, N, K, sa, sb, so, binding.LAYOUTS["nt"], 0, None)
         assert st == want, (batch, sa, sb, so, st)
+
+
+def test_preact_argument_checks():
+    """mm_linear_preact rejects, before any HIP call: a non-GELU epilogue, a
+    null or overlapping pre-activation output."""
+    lib = binding.load()
+    x, W, bias, out, pre = 4096, 8192, 1 << 20, 1 << 30, 1 << 31  # fake disjoint addresses
+    M, N, K = 64, 64, 64
+    nt = binding.LAYOUTS["nt"]
+    E = binding.EPILOGUES
+    cases = [
+        (pre, E["bias"], binding.MM_ERR_INVALID_VALUE),           # no activation to precede
+        (pre, E["none"], binding.MM_ERR_INVALID_VALUE),
+        (None, E["bias_gelu_tanh"], binding.MM_ERR_INVALID_VALUE),  # null preact
+        (out + 64, E["bias_gelu_tanh"], binding.MM_ERR_INVALID_VALUE),  # overlaps out
+        (x + 2, E["gelu_tanh"], binding.MM_ERR_INVALID_VALUE),   # overlaps x
+        (pre + 1, E["bias_gelu_tanh"], binding.MM_ERR_MISALIGNED),  # not element aligned
+    ]
+    for p, epi, want in cases:
+        st = lib.mm_linear_preact(x, W, bias, out, p, M, N, K, nt, epi, None)
+        assert st == want, (p, epi, st)
+    # an empty product is a successful no-op
+    assert lib.mm_linear_preact(x, W, bias, out, pre, 0, N, K, nt, E["bias_gelu_tanh"], None) == 0

@@ -241,6 +241,63 @@ def test_batched_torch_views_and_linear(dev):
 # (M, N, K, configuration): few 256 x 256 output tiles, long K.  The forced
 # slice counts with small grids make slices wait on other workgroups across
 # rounds of work units.
+# ------------------------------------------------ two outputs: GELU and its input
+def call_linear_preact(A, B, bias, M, N, K, layout, epi, out, pre):
+    lib = binding.load()
+    st = lib.mm_linear_preact(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None,
+                              out.data_ptr(), pre.data_ptr(), M, N, K, binding.LAYOUTS[layout],
+                              binding.EPILOGUES[epi], stream())
+    binding.check(st, "mm_linear_preact")
+
+
+# (M, N, K, layout): slab kernel (interior and edge tiles), ragged K and the
+# [K][N] weight layout (basic kernel)
+PREACT_CASES = [(512, 512, 256, "nt"), (300, 267, 192, "nt"), (257, 139, 200, "nt"),
+                (129, 136, 72, "nn"), (520, 392, 4160, "nt")]
+
+
+@pytest.mark.parametrize("case", range(len(PREACT_CASES)))
+def test_preact_mapping_bitexact(dev, case):
+    """Integer operands: the pre-activation (bias included) is exact in fp32
+    and bf16, so it must match the oracle's bias epilogue bit for bit; the
+    GELU output is checked against the oracle's bias+GELU within 2e-2."""
+    M, N, K, layout = PREACT_CASES[case]
+    say("preact mapping", PREACT_CASES[case])
+    ops = synth.mapping_operands(M, N, K, layout, seed=M + 5 * N + K, with_bias=True)
+    A, B, bias = ops["A"], ops["B"], ops["bias"]
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    pre = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    call_linear_preact(A.to(dev), B.to(dev), bias.to(dev), M, N, K, layout, "bias_gelu_tanh", out, pre)
+    torch.cuda.synchronize()
+    _, pre_bits = oracle.gemm(synth.bits(A), synth.bits(B), layout, "bias", bias=synth.bits(bias))
+    np.testing.assert_array_equal(to_bits(pre), pre_bits)
+    y, _ = oracle.gemm(synth.bits(A), synth.bits(B), layout, "bias_gelu_tanh", bias=synth.bits(bias))
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+
+
+@pytest.mark.parametrize("epi", ["gelu_tanh", "bias_gelu_tanh"])
+def test_preact_random_matches_single_output(dev, epi):
+    """Seeded normal data: both outputs within tolerance of the oracle, and
+    bit-identical to the single-output calls (same kernel arithmetic)."""
+    M, N, K = 520, 392, 512
+    say("preact random", epi, (M, N, K))
+    x = synth.randn_bf16((M, K), 1.0, 31).to(dev)
+    W = synth.randn_bf16((N, K), K ** -0.5, 32).to(dev)
+    bias = synth.randn_bf16((N,), 1.0, 33).to(dev) if epi == "bias_gelu_tanh" else None
+    out, pre = mm.linear_preact(x, W, bias, epi)
+    one = mm.linear(x, W, bias, epi)
+    pre_one = mm.linear(x, W, bias, "bias" if bias is not None else "none", workspace=None)
+    torch.cuda.synchronize()
+    bb = synth.bits(bias.cpu()) if bias is not None else None
+    y, _ = oracle.gemm(synth.bits(x.cpu()), synth.bits(W.cpu()), "nt", epi, bias=bb)
+    t, _ = oracle.gemm(synth.bits(x.cpu()), synth.bits(W.cpu()), "nt", "bias" if bb is not None else "none",
+                       bias=bb)
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+    assert tol_excess(pre.float().cpu().numpy(), t, 2e-2) <= 0
+    assert torch.equal(out.view(torch.int16), one.view(torch.int16))
+    assert torch.equal(pre.view(torch.int16), pre_one.view(torch.int16))
+
+
 SK_CASES = [
     (520, 395, 8192, None),
     (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=4"),
