@@ -169,7 +169,14 @@ def main() -> int:
     traffic = traffic_from_profile(name)
     tiles = binding.describe_config(w.form, w.M, w.N, w.K, w.layout)
     cfg = dict(kv.split("=") for kv in tiles.split(","))
-    kernel = f"mmk::{cfg['KERNEL']}<{cfg['BM']},{cfg['BN']},{cfg['WM']},{cfg['WN']},{w.form == 'ffn'}>"
+    ffn = str(w.form == "ffn").lower()
+    if cfg["KERNEL"] == "gemm_nt_slab":  # <tile, waves, FFN, split-K, pre-activation output>
+        splitk = (w.form != "ffn" and w.epilogue == "none"
+                  and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
+        kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
+                  f"{str(splitk).lower()}, false>")
+    else:
+        kernel = f"mmk::{cfg['KERNEL']}<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}>"
     result = {
         "metric": "TFLOP/s and % of bf16 MFMA peak, 8192^3 linear+bias+GELU, 1 GPU"
         if name == synth.HEADLINE else f"TFLOP/s, {name}, 1 GPU",
