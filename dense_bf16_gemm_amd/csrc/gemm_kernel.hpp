@@ -79,20 +79,30 @@ struct GemmParams {
   int group_m;           // band height of the grouped tile order, in tiles
   int xcd_remap;
   int k_alt;             // alternate K direction per persistent tile
-  // Split-K (gemm_nt_slab with SPLITK): work unit u = s * num_tiles + t runs
-  // super-steps [s*KS/S, (s+1)*KS/S) of tile t.  Slices 0..S-2 leave fp32
-  // partial tiles in the workspace and raise a flag; slice S-1 waits for them,
-  // adds them in slice order and runs the epilogue.
+  // Stream-K (gemm_nt_slab with SPLITK): each tile's K loop is cut into
+  // sk_chunks chunks (chunk j: super-steps [j*KS/n, (j+1)*KS/n)); the
+  // num_tiles * n chunks, tile-major, are dealt to the workgroups in
+  // contiguous ranges of sk_items (<= n) chunks.  A range covers the tail of
+  // one tile and/or the head of the next.  The workgroup holding a tile's
+  // chunk 0 owns the tile: the others (always the first piece of their
+  // range) leave fp32 partial tiles in their workgroup's slot and raise its
+  // flag; the owner (always the last piece of its range) waits for them and
+  // adds them in k order.  sk_items == 0 selects chunk-major split-K instead:
+  // workgroup c runs chunk c / num_tiles of tile c % num_tiles, so that
+  // workgroups running at once cover neighbouring tiles at the same k (they
+  // share operand panels in L2); the owner's partners are c + num_tiles,
+  // c + 2 num_tiles, ...
   // Batched form: `batch` independent products; operand / output bases of
   // entry b are b * stride elements past entry 0 (a stride of 0 broadcasts).
   // The persistent loop walks batch * num_tiles units, unit u being tile
   // u % num_tiles of entry u / num_tiles.
   int batch;             // >= 1
   int64_t stride_a, stride_b, stride_out;
-  int sk_slices;         // S (1 = off)
+  int sk_chunks;         // n (1 = off)
+  int sk_items;          // chunks per workgroup range (0: chunk-major, one each)
   uint32_t sk_epoch;     // flag value of this launch (never 0)
-  float* sk_part;        // [num_tiles][S-1][256*256] partial tiles
-  uint32_t* sk_flag;     // [num_tiles][S-1]
+  float* sk_part;        // [grid][256*256] partial tiles, one slot per workgroup
+  uint32_t* sk_flag;     // [grid]
 };
 
 // Schedule helpers, shared with the host so that it can describe the order.

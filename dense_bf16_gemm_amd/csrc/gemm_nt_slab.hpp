@@ -149,12 +149,19 @@ gemm_nt_slab(GemmParams p) {
   // wave-uniform results back to scalar registers, so that all descriptor
   // and offset arithmetic below stays scalar)
   const int wg = __builtin_amdgcn_readfirstlane(remap_workgroup(blockIdx.x, G, p.xcd_remap));
-  // work units: tiles, or (split-K) tile slices, slice-major
-  const int S = SPLITK ? p.sk_slices : 1;
-  const int units = p.num_tiles * S * (SPLITK ? 1 : p.batch);
-  if (wg >= units) return;
-  const int my_tiles = __builtin_amdgcn_readfirstlane((units - wg + G - 1) / G);
   const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
+  // work units: tiles (of every batch entry), or (stream-K) the one or two
+  // pieces of this workgroup's chunk range [ci0, ci1)
+  // (sk_items == 0: chunk-major split-K, workgroup c runs chunk c / tiles of
+  // tile c % tiles, one unit)
+  const int SKN = SPLITK ? p.sk_chunks : 1;
+  const bool sk_cmaj = SPLITK && p.sk_items == 0;
+  const int ci0 = SPLITK ? (sk_cmaj ? wg : wg * p.sk_items) : 0;
+  const int ci1 = SPLITK ? (sk_cmaj ? wg + 1 : min(ci0 + p.sk_items, p.num_tiles * SKN)) : 0;
+  const int units = SPLITK ? 0 : p.num_tiles * p.batch;
+  if (SPLITK ? ci1 > p.num_tiles * SKN || ci0 >= ci1 : wg >= units) return;
+  const int my_tiles = __builtin_amdgcn_readfirstlane(
+      SPLITK ? (sk_cmaj ? 1 : (ci1 - 1) / SKN - ci0 / SKN + 1) : (units - wg + G - 1) / G);
   const int M = p.M, N = p.N, K = p.K;
   const int64_t ld = K;
 
@@ -177,18 +184,28 @@ gemm_nt_slab(GemmParams p) {
     int alt;
     int kbeg;  // first super-step of a split-K slice (0 otherwise)
   };
-  // output tile, split-K slice or batch entry, and first and count of
-  // super-steps of unit u
-  auto unit_of = [&](int u, int* tile, int* slice, int* kbeg, int* nks) __attribute__((always_inline)) {
+  // output tile, batch entry, and first and count of super-steps of this
+  // workgroup's unit i
+  auto unit_of = [&](int i, int* tile, int* slice, int* kbeg, int* nks) __attribute__((always_inline)) {
+    const int u = wg + i * G;
     *tile = u;
     *slice = 0;
     *kbeg = 0;
     *nks = KS;
     if constexpr (SPLITK) {
-      *slice = __builtin_amdgcn_readfirstlane(u / p.num_tiles);
-      *tile = u - *slice * p.num_tiles;
-      *kbeg = __builtin_amdgcn_readfirstlane(*slice * KS / S);
-      *nks = __builtin_amdgcn_readfirstlane((*slice + 1) * KS / S) - *kbeg;
+      // piece i: the chunks of [ci0, ci1) that fall in one tile
+      int t, a;
+      if (sk_cmaj) {
+        a = __builtin_amdgcn_readfirstlane(wg / p.num_tiles);
+        t = wg - a * p.num_tiles;
+      } else {
+        t = __builtin_amdgcn_readfirstlane(ci0 / SKN + i);
+        a = (i == 0 ? ci0 : t * SKN) - t * SKN;
+      }
+      const int b = sk_cmaj ? a + 1 : min(ci1, (t + 1) * SKN) - t * SKN;
+      *tile = t;
+      *kbeg = __builtin_amdgcn_readfirstlane(a * KS / SKN);
+      *nks = __builtin_amdgcn_readfirstlane(b * KS / SKN) - *kbeg;
     } else {
       if (p.batch > 1) {  // slice = batch entry
         *slice = __builtin_amdgcn_readfirstlane(u / p.num_tiles);
@@ -199,7 +216,7 @@ gemm_nt_slab(GemmParams p) {
   auto tile_desc = [&](int tile_i) __attribute__((always_inline)) {
     int tm, tn;
     int tile, slice, kbeg, nks;
-    unit_of(wg + tile_i * G, &tile, &slice, &kbeg, &nks);
+    unit_of(tile_i, &tile, &slice, &kbeg, &nks);
     tile_coords(tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
@@ -532,12 +549,13 @@ gemm_nt_slab(GemmParams p) {
     }
   };
 
-  // Split-K end of a work unit (plain product, no epilogue math), one code
-  // path for every slice: slices 0..S-2 (partial) write their raw fp32 tile
-  // into a 256 x 256 row-major workspace slot; the last slice adds the nadd
-  // slots at `addend` in slot order and writes the output (bounds-checked).
-  auto epilogue_sk = [&](bool partial, float* slot, int m0, int n0, const float* addend, int nadd)
-      __attribute__((always_inline)) {
+  // Split-K / stream-K end of a work unit (plain product, no epilogue math),
+  // one code path for every piece: a piece that does not start its tile
+  // (partial) writes its raw fp32 tile into its 256 x 256 row-major workspace
+  // slot; the owner adds the nadd slots at `addend`, `astride` floats apart,
+  // in k order and writes the output (bounds-checked).
+  auto epilogue_sk = [&](bool partial, float* slot, int m0, int n0, const float* addend, int nadd,
+                         int64_t astride) __attribute__((always_inline)) {
     const int ldo = partial ? 256 : N;
     const int mlim = partial ? 256 : M - m0, nlim = partial ? 256 : N - n0;
     const bool o_f32 = partial || p.out_f32;
@@ -558,7 +576,7 @@ gemm_nt_slab(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) add[j] = 0.f;
         const float* a = addend + ml * 256 + nl;
-        for (int s2 = 0; s2 < nadd; ++s2, a += 65536) {
+        for (int s2 = 0; s2 < nadd; ++s2, a += astride) {
           const f32x4 x0 = reinterpret_cast<const f32x4*>(a)[0];
           const f32x4 x1 = reinterpret_cast<const f32x4*>(a)[1];
           add[0] += x0[0]; add[1] += x0[1]; add[2] += x0[2]; add[3] += x0[3];
@@ -608,7 +626,7 @@ gemm_nt_slab(GemmParams p) {
     // from ks = nks - 2 on the next unit's super-steps 0 and 1.
     const TileDesc nxt = tile_desc(tile_i + 1 < my_tiles ? tile_i + 1 : tile_i);
     int h_tile, h_slice, h_kbeg, nks;
-    unit_of(wg + tile_i * G, &h_tile, &h_slice, &h_kbeg, &nks);
+    unit_of(tile_i, &h_tile, &h_slice, &h_kbeg, &nks);
     __builtin_amdgcn_s_waitcnt(kLgkmDrained);
     for (int ks = 0; ks < nks; ++ks) {
       int lks = ks + 2;
@@ -619,17 +637,22 @@ gemm_nt_slab(GemmParams p) {
       super_step(k0_of(lks));
     }
     if constexpr (SPLITK) {
-      // Slices 0..S-2 leave their raw tile in slot (tile, slice) and raise
-      // its flag; the last slice waits (bounded) for the flags and adds the
-      // slots in slice order.  Release/acquire fences at device scope make
-      // the slots written on one XCD visible on another.
+      // A piece that does not start the tile leaves its raw tile in this
+      // workgroup's slot and raises its flag; the owner (the piece with
+      // chunk 0) waits (bounded) for the flags of the workgroups after it
+      // that hold the rest of the tile, and adds their slots in k order.
+      // Release/acquire fences at device scope make the slots written on one
+      // XCD visible on another.
+      // (Chunk-major: the partners are workgroups wg + T, wg + 2T, ...)
       constexpr int64_t kSlot = 256 * 256;
-      const int nslot = S - 1;
-      const bool partial = h_slice < nslot;
-      float* slots = p.sk_part + (int64_t)h_tile * nslot * kSlot;
+      const bool partial = h_kbeg != 0;
+      const int nadd = partial ? 0
+                       : sk_cmaj ? SKN - 1
+                                 : __builtin_amdgcn_readfirstlane(((h_tile + 1) * SKN - 1) / p.sk_items) - wg;
+      const int cstep = sk_cmaj ? p.num_tiles : 1;
       if (!partial && tid == 0) {
-        for (int s2 = 0; s2 < nslot; ++s2) {
-          const uint32_t* f = p.sk_flag + h_tile * nslot + s2;
+        for (int i2 = 1; i2 <= nadd; ++i2) {
+          const uint32_t* f = p.sk_flag + wg + i2 * cstep;
           for (int spin = 0; spin < (1 << 22); ++spin) {
             if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.sk_epoch) break;
             __builtin_amdgcn_s_sleep(8);
@@ -640,13 +663,12 @@ gemm_nt_slab(GemmParams p) {
       if (!partial) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       int tm, tn;
       tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-      epilogue_sk(partial, slots + (int64_t)h_slice * kSlot, tm * BM, tn * OUT_BN, slots,
-                  partial ? 0 : nslot);
+      epilogue_sk(partial, p.sk_part + (int64_t)wg * kSlot, tm * BM, tn * OUT_BN,
+                  p.sk_part + (int64_t)(wg + cstep) * kSlot, nadd, (int64_t)cstep * kSlot);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __builtin_amdgcn_s_barrier();
       if (partial && tid == 0)
-        __hip_atomic_store(p.sk_flag + h_tile * nslot + h_slice, p.sk_epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.sk_flag + wg, p.sk_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       continue;
     }
 

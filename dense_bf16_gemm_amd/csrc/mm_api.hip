@@ -354,50 +354,79 @@ struct Plan {
 };
 
 // ----------------------------------------------------------------------------
-// Split-K: the pages name splitting the K loop over workgroups (split-K, and
-// stages spread over SMs "a la stream-K") and leave both out of their
-// persistent scheduler (PR "Implement persistent matmul scheduling", review
-// notes).  Here: when a K-contiguous single-weight product has fewer 256 x 256
-// tiles than the grid has workgroups, the slab kernel's K loop is cut into S
-// slices and the units (slice, tile) are spread over the grid; the partial
-// tiles meet in a caller-provided workspace.
+// Split-K / stream-K: the pages name splitting the K loop over workgroups
+// (split-K, and stages spread over SMs "a la stream-K") and leave both out of
+// their persistent scheduler (PR "Implement persistent matmul scheduling",
+// review notes).  Here: when a K-contiguous single-weight product has fewer
+// 256 x 256 tiles than the grid has workgroups, each tile's K loop is cut into
+// n chunks and the tiles * n chunks are dealt to the resident workgroups in
+// equal contiguous ranges (stream-K); the partial tiles meet in a
+// caller-provided workspace.
 // ----------------------------------------------------------------------------
 constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
 
-// plain K-contiguous products (no bias or activation: the slices' sums meet
+// plain K-contiguous products (no bias or activation: the pieces' sums meet
 // before any epilogue math would apply)
 bool splitk_shape(const Request& r) {
   return r.batch == 1 && !r.ffn && r.epi == mmk::EPI_NONE && r.layout == MM_NT && r.K % mmk::kSlabK == 0 &&
          r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31);
 }
 
-// Slices for a grid of `wgs` resident workgroups (1 = no split).
-int splitk_slices(const Request& r, const Config& c, int64_t wgs) {
-  if (c.sk == 1 || !splitk_shape(r)) return 1;
+struct SkPlan {
+  int n = 1;        // chunks per tile (1 = no split)
+  int q = 0;        // chunks per workgroup range; 0 = chunk-major, one per workgroup
+  int64_t wgs = 0;  // workgroups with work (the grid)
+};
+
+// Chunks and their dealing for `wgs` resident workgroups.  Automatic: only
+// when every tile can take two chunks (2 T <= wgs), dealt chunk-major, one
+// per workgroup: workgroups running side by side then read the same k range
+// of neighbouring tiles' panels.  Dealt tile-major in ranges (stream-K), the
+// k positions of neighbouring workgroups no longer match and their L2
+// sharing is lost: 2047 x 3001 x 65536 (96 tiles on 256 CUs) 720 us
+// chunk-major vs 785 us in ranges of 3/8 of a tile; 3584 x 3584 x 16384
+// (196 tiles) 320 us unsplit vs 538 us in ranges of 7/8 of a tile.  Stream-K
+// stays available through a forced chunk count (SK=n with n T > wgs).
+SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
+  SkPlan sp;
+  if (c.sk == 1 || !splitk_shape(r)) return sp;
   const int64_t T = cdiv(r.M, 256) * cdiv(r.N, 256);
   const int64_t KS = r.K / mmk::kSlabK;
-  if (c.sk >= 2) return KS / c.sk >= 2 ? c.sk : 1;
-  if (T >= wgs) return 1;
-  // Fewest slices that occupy three quarters of the grid: more slices read
-  // the operands from more places at once and were slower (2047 x 3001 x
-  // 65536, 96 tiles on 256 CUs: 2 slices 745 us, 4: 941, 5: 849, 8: 948,
-  // 16: 1287; unsplit 1165).
-  int S = (int)cdiv(3 * wgs, 4 * T);
-  if (S < 2) S = 2;
-  if (S > 16) S = 16;
-  while (S > 2 && KS / S < 8) --S;
-  return KS / S >= 2 ? S : 1;
+  int n;
+  if (c.sk >= 2) {
+    n = c.sk;
+    if (KS / n < 2) return sp;  // a piece runs at least two super-steps
+  } else if (2 * T <= wgs) {
+    // fewest chunks that occupy three quarters of the grid: more chunks read
+    // the operands from more places at once and were slower (2 chunks 745 us,
+    // 4: 941, 5: 849, 8: 948, 16: 1287; unsplit 1165)
+    n = (int)cdiv(3 * wgs, 4 * T);
+    if (n > 16) n = 16;
+    while (n > 2 && (KS / n < 8 || n * T > wgs)) --n;
+    if (KS / n < 2) return sp;
+  } else {
+    return sp;
+  }
+  sp.n = n;
+  if (n * T <= wgs) {  // chunk-major, one chunk per workgroup
+    sp.q = 0;
+    sp.wgs = n * T;
+    return sp;
+  }
+  const int64_t q = cdiv(T * n, wgs);
+  if (q >= n) return SkPlan();  // every range would be a whole tile
+  sp.q = (int)q;
+  sp.wgs = cdiv(T * n, q);
+  return sp;
 }
 
-int64_t splitk_ws_bytes(const Request& r, int S) {
-  if (S <= 1) return 0;
-  const int64_t slots = cdiv(r.M, 256) * cdiv(r.N, 256) * (S - 1);
-  const int64_t flags = cdiv(slots * 4, 256) * 256;
-  return flags + slots * kSkSlotBytes;
+int64_t splitk_ws_bytes(const SkPlan& sp) {
+  if (sp.n <= 1) return 0;
+  return cdiv(sp.wgs * 4, 256) * 256 + sp.wgs * kSkSlotBytes;
 }
 
-// Work units of a split-K launch run on this many workgroups, all resident
-// at once (a last slice waits for the others).
+// Work units of a stream-K launch run on this many workgroups, all resident
+// at once (an owner waits for the workgroups after it).
 int64_t splitk_wgs(const Config& c, int cus, int occ) {
   const int64_t resident = (int64_t)cus * occ;
   return c.grid > 0 && c.grid < resident ? c.grid : resident;
@@ -406,20 +435,21 @@ int64_t splitk_wgs(const Config& c, int cus, int occ) {
 std::atomic<uint32_t> g_sk_epoch{0};
 
 // Everything but the device-dependent grid size; no HIP calls.
-mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
+mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan& sp = SkPlan()) {
+  const bool sk = sp.n > 1;
   const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
   if (r.ffn && !b_kc) return fail(MM_ERR_UNSUPPORTED, "FFN weights must be [N][K]");
   Config c = c_in;
   KernelEntry* k = nullptr;
-  if (S > 1) {
+  if (sk) {
     c.bm = c.bn = 256;
     c.wgm = c.wgn = 2;
     k = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
   }
   // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
-  for (int fam = c.pipe; fam >= 0 && !k && S <= 1; --fam) {
+  for (int fam = c.pipe; fam >= 0 && !k && !sk; --fam) {
     if (fam > 0 && span >= (int64_t(1) << 31)) continue;
     // the batched form and the pre-activation output run on the slab and
     // basic kernels
@@ -467,13 +497,13 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, int S = 1) {
   p.group_m = c.group;
   p.xcd_remap = c.xcd;
   p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
-  p.sk_slices = 1;
-  if (S > 1) {
+  p.sk_chunks = 1;
+  if (sk) {
     p.k_alt = 0;
-    p.sk_slices = S;
-    const int64_t slots = (int64_t)p.num_tiles * (S - 1);
+    p.sk_chunks = sp.n;
+    p.sk_items = sp.q;
     p.sk_flag = static_cast<uint32_t*>(r.ws);
-    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + cdiv(slots * 4, 256) * 256);
+    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + cdiv(sp.wgs * 4, 256) * 256);
   }
   pl->kernel = k;
   pl->threads = k->wgm * k->wgn * 64;  // the selected kernel's block size
@@ -487,6 +517,7 @@ mm_status run(const Request& r, void* stream) {
   if (r.M == 0 || r.N == 0) return MM_OK;
   const Config c = choose_config(r.ffn, r.M, r.N, r.K);
   Plan pl;
+  SkPlan sp;
   s = plan_host(r, c, &pl);
   if (s != MM_OK) return s;
   int cus = 0, occ = 0;
@@ -496,27 +527,27 @@ mm_status run(const Request& r, void* stream) {
     int sk_occ = 0;
     KernelEntry* sk = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
     if ((s = kernel_occupancy(sk, &sk_occ)) != MM_OK) return s;
-    const int S = splitk_slices(r, c, splitk_wgs(c, cus, sk_occ));
-    if (S > 1) {
-      if (r.ws_bytes < splitk_ws_bytes(r, S))
+    sp = splitk_plan(r, c, splitk_wgs(c, cus, sk_occ));
+    if (sp.n > 1) {
+      if (r.ws_bytes < splitk_ws_bytes(sp))
         return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
       if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-      if ((s = plan_host(r, c, &pl, S)) != MM_OK) return s;
+      if ((s = plan_host(r, c, &pl, sp)) != MM_OK) return s;
       uint32_t e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
       if (e == 0) e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
       pl.p.sk_epoch = e;
     }
   }
   if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
-  const int64_t units = (int64_t)pl.p.num_tiles * pl.p.sk_slices * pl.p.batch;
+  const int64_t units = (int64_t)pl.p.num_tiles * pl.p.batch;
   int64_t grid = c.grid > 0 ? c.grid : (int64_t)cus * occ;
-  if (pl.p.sk_slices > 1 && grid > (int64_t)cus * occ) grid = (int64_t)cus * occ;
   if (grid > units) grid = units;
+  if (sp.n > 1) grid = sp.wgs;  // one chunk range per workgroup, all resident
   if (std::getenv("MM_LOG"))
     std::fprintf(stderr, "libmm: M=%lld N=%lld K=%lld layout=%d ffn=%d -> BM=%d BN=%d WM=%d WN=%d G=%d "
-                 "XCD=%d KALT=%d grid=%lld tiles=%d slices=%d\n", (long long)r.M, (long long)r.N,
+                 "XCD=%d KALT=%d grid=%lld tiles=%d chunks=%d\n", (long long)r.M, (long long)r.N,
                  (long long)r.K, r.layout, (int)r.ffn, c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd,
-                 pl.p.k_alt, (long long)grid, pl.p.num_tiles, pl.p.sk_slices);
+                 pl.p.k_alt, (long long)grid, pl.p.num_tiles, pl.p.sk_chunks);
   void* args[] = {&pl.p};
   hipError_t e = hipLaunchKernel(pl.kernel->fn, dim3((unsigned)grid), dim3(pl.threads), args, 0,
                                  static_cast<hipStream_t>(stream));
@@ -618,7 +649,7 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
   if ((s = device_cus(&cus)) != MM_OK) return s;
   if ((s = kernel_occupancy(find_kernel(256, 256, 2, 2, true, true, false, 3, true), &occ)) != MM_OK)
     return s;
-  *bytes = splitk_ws_bytes(r, splitk_slices(r, c, splitk_wgs(c, cus, occ)));
+  *bytes = splitk_ws_bytes(splitk_plan(r, c, splitk_wgs(c, cus, occ)));
   return MM_OK;
 }
 

@@ -151,8 +151,10 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * there and left out of the persistent scheduler).  When a plain K-contiguous
  * (MM_NT) product -- mm_matmul, or mm_linear with MM_EPI_NONE -- with K a
  * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
- * workgroups, the _ws entry points below cut each tile's K loop into slices
- * spread over the grid; the fp32 partial tiles meet in this workspace.
+ * workgroups, the _ws entry points below cut each tile's K loop into chunks
+ * and deal the chunks of all tiles to the resident workgroups in equal
+ * contiguous ranges (stream-K); the fp32 partial tiles meet in this workspace
+ * (one 256 KiB slot and one flag per workgroup).
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
  *   bytes   receives the size a call of this shape on the current device may
  *           use; 0 = the shape runs without one.  Queries the device (CU
@@ -168,9 +170,9 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
  * workspace, or a shape that needs none, they behave exactly as mm_matmul /
  * mm_linear.  A workspace smaller than reported returns MM_ERR_INVALID_VALUE;
  * one that overlaps an operand or the output returns MM_ERR_INVALID_VALUE.
- * Still one kernel per call; the slices' partial sums are added in slice
- * order, so results are reproducible run to run (they differ from the
- * unsplit kernel's by fp32 rounding order only).                           */
+ * Still one kernel per call; a tile's partial sums are added in k order, so
+ * results are reproducible run to run (they differ from the unsplit
+ * kernel's by fp32 rounding order only).                                   */
 mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
                        mm_layout layout, mm_out_dtype out_dtype, void* workspace,
                        int64_t workspace_bytes, void* stream);
@@ -196,8 +198,8 @@ mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* 
  * direction per persistent tile (1), never (0) or automatically (2);
  * GRID: persistent grid size, 0 = one wave of resident workgroups; PIPE:
  * preferred kernel family, 3 whole-line slab ring, 2 ping-pong, 1 32-k
- * pipeline, 0 basic; SK: split-K slices when a workspace is given, 0
- * automatic, 1 never, n >= 2 forced).  The
+ * pipeline, 0 basic; SK: stream-K chunks per tile when a workspace is
+ * given, 0 automatic, 1 never, n >= 2 forced).  The
  * heuristic is replaced for every later call in the process, in the manner
  * of the pages' heuristic plugin (PR "Translate MmaOp patterns properly on
  * Hopper", review of MatmulSchedulerPluginTest).  NULL or "" restores the

@@ -298,10 +298,15 @@ def test_preact_random_matches_single_output(dev, epi):
     assert torch.equal(pre.view(torch.int16), pre_one.view(torch.int16))
 
 
+# (M, N, K, config): automatic chunk-major (16 chunks per tile, one per
+# workgroup); forced stream-K on 140 tiles (ranges of 3/4 of a tile);
+# ranges of two chunks of three that cross tile boundaries; ranges of
+# three of four; uneven chunk-major chunks (64 super-steps in 7)
 SK_CASES = [
     (520, 395, 8192, None),
-    (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=4"),
-    (257, 520, 1024, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=0,KALT=2,SK=2,GRID=2"),
+    (2560, 3584, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=4"),
+    (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6"),
+    (257, 520, 1024, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=0,KALT=2,SK=4,GRID=10"),
     (64, 8, 4096, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=7"),
 ]
 
