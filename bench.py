@@ -175,6 +175,8 @@ def main() -> int:
                   and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
                   f"{str(splitk).lower()}, false>")
+    elif cfg["KERNEL"] == "gemm_ws":
+        kernel = "mmk::gemm_ws"
     else:
         kernel = f"mmk::{cfg['KERNEL']}<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}>"
     result = {

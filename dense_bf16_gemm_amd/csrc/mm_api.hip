@@ -22,6 +22,7 @@
 #include "gemm_kernel.hpp"
 #include "gemm_nt_pipe.hpp"
 #include "gemm_pingpong.hpp"
+#include "gemm_ws.hpp"
 #include "gemm_nt_slab.hpp"
 
 namespace {
@@ -39,7 +40,8 @@ mm_status fail(mm_status s, const std::string& msg) {
 struct KernelEntry {
   int bm, bn, wgm, wgn;
   bool a_kc, b_kc, ffn;
-  int pipe;  // 3: whole-line slab ring (gemm_nt_slab), 2: ping-pong (gemm_pingpong),
+  int pipe;  // 4: wave-specialized (gemm_ws), 3: whole-line slab ring (gemm_nt_slab),
+             // 2: ping-pong (gemm_pingpong),
              // 1: K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
   const void* fn;
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
@@ -72,6 +74,9 @@ struct KernelEntry {
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, true>), {0}, \
    false, true}
 
+#define MM_KWS()                                                                           \
+  {256, 128, 2, 4, true, true, false, 4, reinterpret_cast<const void*>(&mmk::gemm_ws), {0}}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
@@ -79,6 +84,7 @@ struct KernelEntry {
 KernelEntry g_kernels[] = {
     MM_KSK(),
     MM_KSP(),
+    MM_KWS(),
     MM_KS(false),
     MM_KS(true),
     MM_KPP(false),
@@ -119,7 +125,8 @@ struct Config {
   int xcd = 1;    // XCD-aware remap
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
-  int pipe = 3;   // preferred kernel family: 3 slab ring, 2 ping-pong, 1 pipeline, 0 basic
+  int pipe = 3;   // preferred kernel family: 4 wave-specialized (BN=128, WN=4), 3 slab ring,
+                  // 2 ping-pong, 1 pipeline, 0 basic
   int sk = 0;     // split-K slices when a workspace is given: 0 automatic, 1 off, n forced
 };
 
@@ -156,7 +163,7 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "SK") c.sk = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 3 || c.sk > 64) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 4 || c.sk > 64) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -447,6 +454,16 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     c.wgm = c.wgn = 2;
     k = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
   }
+  // the wave-specialized kernel (a configuration override for comparison)
+  // takes single-weight K-contiguous products with whole super-steps; other
+  // shapes run the default tile under that override
+  if (c.pipe == 4 && !(b_kc && a_kc && !r.ffn && r.batch == 1 && !r.out_pre && !sk &&
+                       r.K % mmk::kSlabK == 0 && r.K >= 2 * mmk::kSlabK &&
+                       (int64_t)256 * r.K * 2 < (int64_t(1) << 31))) {
+    c.bm = c.bn = 256;
+    c.wgm = c.wgn = 2;
+    c.pipe = 3;
+  }
   // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k && !sk; --fam) {
@@ -490,7 +507,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   p.num_tiles = (int)(tm * tn);
   // the pipelined kernel runs k-steps of 32 in pairs: an even count, padded
   // with k-steps past K that read zeros
-  p.k_tiles = k->pipe == 3 ? (int)cdiv(r.K, mmk::kSlabK)
+  p.k_tiles = k->pipe >= 3 ? (int)cdiv(r.K, mmk::kSlabK)
              : k->pipe == 2 ? (int)cdiv(r.K, mmk::kPipeBK)
              : k->pipe == 1 ? (int)(2 * cdiv(r.K, 2 * mmk::kPipeBK))
                             : (int)cdiv(r.K, mmk::kBK);
@@ -720,7 +737,8 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
               false, form == 1};
     Plan pl;
     if (plan_host(r, c, &pl) == MM_OK)
-      kernel = pl.kernel->pipe == 3   ? "gemm_nt_slab"
+      kernel = pl.kernel->pipe == 4   ? "gemm_ws"
+               : pl.kernel->pipe == 3 ? "gemm_nt_slab"
                : pl.kernel->pipe == 2 ? "gemm_pingpong"
                : pl.kernel->pipe      ? "gemm_nt_pipe"
                                       : "gemm_persistent";

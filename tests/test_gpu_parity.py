@@ -31,6 +31,10 @@ CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     "BM=256,BN=256,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=2",
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=1",
+    # wave-specialized producer/consumer kernel (256 x 128 tiles), and with a
+    # small grid so that the ring runs across several tiles per workgroup
+    "BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=4",
+    "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=4",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
 ]
@@ -120,6 +124,19 @@ def shapes_for(layout):
             N = N + 3
         out.append((M, N, K))
     return out
+
+
+def test_ws_config_selects_ws_kernel():
+    """PIPE=4 runs the wave-specialized kernel where it applies and the default
+    slab tile elsewhere (ragged K, FFN)."""
+    binding.set_config("BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=4")
+    try:
+        for (M, N, K) in shapes_for("nt")[-3:]:
+            assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_ws")
+        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_pipe")
+        assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
+    finally:
+        binding.set_config(None)
 
 
 def test_slab_shapes_select_slab_kernel():
