@@ -32,9 +32,13 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 
+# the headers the slab kernel (every benchmarked workload's kernel) is built from
+SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(n for n in os.listdir(CSRC) if n.endswith(".hpp")):  # the kernel templates
+    for name in SLAB_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
