@@ -371,6 +371,11 @@ struct Plan {
 // caller-provided workspace.
 // ----------------------------------------------------------------------------
 constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
+// The flags always occupy the first 4 KiB of a workspace (one per workgroup,
+// at most 1024), so that a later call of another shape never reads a flag
+// from bytes an earlier call used for partial tiles.
+constexpr int64_t kSkFlagBytes = 4096;
+constexpr int64_t kSkMaxWgs = kSkFlagBytes / 4;
 
 // plain K-contiguous products (no bias or activation: the pieces' sums meet
 // before any epilogue math would apply)
@@ -396,7 +401,7 @@ struct SkPlan {
 // stays available through a forced chunk count (SK=n with n T > wgs).
 SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
   SkPlan sp;
-  if (c.sk == 1 || !splitk_shape(r)) return sp;
+  if (c.sk == 1 || !splitk_shape(r) || wgs > kSkMaxWgs) return sp;
   const int64_t T = cdiv(r.M, 256) * cdiv(r.N, 256);
   const int64_t KS = r.K / mmk::kSlabK;
   int n;
@@ -429,7 +434,7 @@ SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
 
 int64_t splitk_ws_bytes(const SkPlan& sp) {
   if (sp.n <= 1) return 0;
-  return cdiv(sp.wgs * 4, 256) * 256 + sp.wgs * kSkSlotBytes;
+  return kSkFlagBytes + sp.wgs * kSkSlotBytes;
 }
 
 // Work units of a stream-K launch run on this many workgroups, all resident
@@ -520,7 +525,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     p.sk_chunks = sp.n;
     p.sk_items = sp.q;
     p.sk_flag = static_cast<uint32_t*>(r.ws);
-    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + cdiv(sp.wgs * 4, 256) * 256);
+    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + kSkFlagBytes);
   }
   pl->kernel = k;
   pl->threads = k->wgm * k->wgn * 64;  // the selected kernel's block size

@@ -154,7 +154,7 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * workgroups, the _ws entry points below cut each tile's K loop into chunks
  * and deal the chunks of all tiles to the resident workgroups in equal
  * contiguous ranges (stream-K); the fp32 partial tiles meet in this workspace
- * (one 256 KiB slot and one flag per workgroup).
+ * (4 KiB of flags, then one 256 KiB slot per workgroup).
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
  *   bytes   receives the size a call of this shape on the current device may
  *           use; 0 = the shape runs without one.  Queries the device (CU

@@ -364,6 +364,37 @@ def test_splitk_mapping_bitexact(dev, case, out_f32):
         binding.set_config(None)
 
 
+def test_splitk_workspace_shared_across_shapes(dev):
+    """One workspace, calls of two shapes with different workgroup counts and
+    dealings alternating (chunk-major 16 chunks on 6 tiles; stream-K ranges on
+    4 tiles): each call's flags sit where the other's never put partial tiles,
+    so every result keeps the oracle's bits."""
+    cases = [(520, 395, 8192, None), (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")]
+    sizes = []
+    for (M, N, K, cfg) in cases:
+        binding.set_config(cfg)
+        sizes.append(binding.workspace_size("matmul", M, N, K))
+    binding.set_config(None)
+    assert min(sizes) > 0
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=dev)
+    ops = []
+    for (M, N, K, cfg) in cases:
+        A, B = synth.dense_int_operands(M, N, K, "nt", seed=7 * M + N + K)
+        _, bits = oracle.gemm(synth.bits(A), synth.bits(B), "nt")
+        ops.append((A.to(dev), B.to(dev), bits))
+    for rep in range(3):
+        for (M, N, K, cfg), (A, B, bits) in zip(cases, ops):
+            say("shared workspace", rep, (M, N, K), cfg)
+            binding.set_config(cfg)
+            try:
+                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                call_matmul_ws(A, B, M, N, K, False, out, ws, ws.numel())
+                torch.cuda.synchronize()
+            finally:
+                binding.set_config(None)
+            np.testing.assert_array_equal(to_bits(out), bits)
+
+
 def test_splitk_random_and_fallbacks(dev):
     M, N, K = 700, 900, 16384
     x = synth.randn_bf16((M, K), 1.0, 11).to(dev)
