@@ -112,6 +112,19 @@ __device__ __forceinline__ void spread_first_row_b() {
   __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
 }
 
+// Last row of a super-step: 2, 2 and 1 scalar instructions after its first
+// three MFMAs, the row's LDS read after the fourth.
+__device__ __forceinline__ void spread_loop_latch() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+
 // SiLU as g / (1 + 2^(-g log2 e)).
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
@@ -426,9 +439,16 @@ gemm_nt_slab(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(r, 1, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      read_a(r, 0, a_nxt);
-      __builtin_amdgcn_sched_barrier(0);
+      if (p == FM - 1) {
+        // last row: the loop's own scalar bookkeeping (counter, compare,
+        // carried unit) goes between its MFMAs instead of after them
+        read_a(r, 0, a_nxt);
+        spread_loop_latch();
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(r, 0, a_nxt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     cur_unit = nua;
     a_cur = a_nxt;
