@@ -10,6 +10,7 @@ in TFLOP/s (2*M*N*K flops per GEMM) once the clocks have settled (the
 first launches after idle run at boost clocks, then the board's power limit
 takes over within about 100 launches), a roofline object for the GEMM kernel
 (achieved TFLOP/s from HIP events around every launch on the launch stream,
+in a second pass of the same number of launches after the timed region,
 against the bf16 dense MFMA peak) and the CPU oracle's throughput on a
 bounded sample of the same workload, timed on this host's cores.
 """
@@ -149,22 +150,29 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     stream = torch.cuda.current_stream()  # the stream every launch goes to
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: the K steps back to back, with one event pair around all
+    # of them (events between launches would add their own gaps to it).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     whole0 = torch.cuda.Event(enable_timing=True)
     whole1 = torch.cuda.Event(enable_timing=True)
     whole0.record(stream)
+    for _ in range(args.steps):
+        step()
+    whole1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = whole0.elapsed_time(whole1)
+    # Then the same number of launches again, each between its own events, for
+    # the kernel's mean launch duration (the roofline figure).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
-    whole1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
-    ms_total = whole0.elapsed_time(whole1)
     ms_per_step = ms_total / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     mean_launch = statistics.fmean(per_launch)
