@@ -79,19 +79,16 @@ struct GemmParams {
   int group_m;           // band height of the grouped tile order, in tiles
   int xcd_remap;
   int k_alt;             // alternate K direction per persistent tile
-  // Stream-K (gemm_nt_slab with SPLITK): each tile's K loop is cut into
-  // sk_chunks chunks (chunk j: super-steps [j*KS/n, (j+1)*KS/n)); the
-  // num_tiles * n chunks, tile-major, are dealt to the workgroups in
-  // contiguous ranges of sk_items (<= n) chunks.  A range covers the tail of
-  // one tile and/or the head of the next.  The workgroup holding a tile's
-  // chunk 0 owns the tile: the others (always the first piece of their
-  // range) leave fp32 partial tiles in their workgroup's slot and raise its
-  // flag; the owner (always the last piece of its range) waits for them and
-  // adds them in k order.  sk_items == 0 selects chunk-major split-K instead:
-  // workgroup c runs chunk c / num_tiles of tile c % num_tiles, so that
-  // workgroups running at once cover neighbouring tiles at the same k (they
-  // share operand panels in L2); the owner's partners are c + num_tiles,
-  // c + 2 num_tiles, ...
+  // Split-K / stream-K (gemm_nt_slab with SPLITK): each tile's K loop is cut
+  // into sk_chunks chunks (chunk j: super-steps [j*KS/n, (j+1)*KS/n)).
+  // sk_items == 0 (chunk-major): workgroup c runs chunk c / num_tiles of tile
+  // c % num_tiles, so that workgroups running at once cover neighbouring
+  // tiles at the same k (they share operand panels in L2).  sk_items = q > 0
+  // (stream-K): the num_tiles * n chunks, tile-major, are dealt to the
+  // workgroups in contiguous ranges of q (< n) chunks; a range covers the
+  // tail of one tile and/or the head of the next.  Every piece writes its
+  // raw fp32 partial tile into its own workspace slot; splitk_reduce adds
+  // them in k order afterwards.
   // Batched form: `batch` independent products; operand / output bases of
   // entry b are b * stride elements past entry 0 (a stride of 0 broadcasts).
   // The persistent loop walks batch * num_tiles units, unit u being tile
@@ -100,9 +97,20 @@ struct GemmParams {
   int64_t stride_a, stride_b, stride_out;
   int sk_chunks;         // n (1 = off)
   int sk_items;          // chunks per workgroup range (0: chunk-major, one each)
-  uint32_t sk_epoch;     // flag value of this launch (never 0)
-  float* sk_part;        // [grid][256*256] partial tiles, one slot per workgroup
-  uint32_t* sk_flag;     // [grid]
+  float* sk_part;        // partial tiles of 256*256 floats: slot wg (chunk-major)
+                         // or 2 wg + piece (stream-K)
+};
+
+// The split-K reduction's arguments (the same tiles, order and dealing as
+// the GemmParams of the launch before it).
+struct SkReduceParams {
+  const float* part;
+  void* out;
+  int M, N;
+  int tiles_m, tiles_n, num_tiles, group_m;
+  int chunks;  // n
+  int items;   // q, 0 = chunk-major
+  int out_f32, out_vec;
 };
 
 // Schedule helpers, shared with the host so that it can describe the order.

@@ -574,70 +574,32 @@ gemm_nt_slab(GemmParams p) {
     }
   };
 
-  // Split-K / stream-K end of a work unit (plain product, no epilogue math),
-  // one code path for every piece: a piece that does not start its tile
-  // (partial) writes its raw fp32 tile into its 256 x 256 row-major workspace
-  // slot; the owner adds the nadd slots at `addend`, `astride` floats apart,
-  // in k order and writes the output (bounds-checked).
-  auto epilogue_sk = [&](bool partial, float* slot, int m0, int n0, const float* addend, int nadd,
-                         int64_t astride) __attribute__((always_inline)) {
-    const int ldo = partial ? 256 : N;
-    const int mlim = partial ? 256 : M - m0, nlim = partial ? 256 : N - n0;
-    const bool o_f32 = partial || p.out_f32;
-    char* obase = partial ? reinterpret_cast<char*>(slot)
-                          : reinterpret_cast<char*>(p.out) + ((int64_t)m0 * N + n0) * (o_f32 ? 4 : 2);
-    const bool vec_ok = partial || p.out_vec;
+  // Split-K / stream-K end of a work unit: the piece's raw fp32 sums go to
+  // its own 256 x 256 row-major workspace slot (every element of the tile,
+  // rows and columns past M and N included: they hold zeros).  The pieces
+  // meet in splitk_reduce, launched after this kernel on the same stream, so
+  // no workgroup waits for another and no cross-XCD cache maintenance is
+  // needed inside the kernel.
+  auto epilogue_part = [&](float* slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
       for (int pr = 0; pr < PAIRS; ++pr) {
         const int ml = wrow_a + lx + 16 * fm;      // tile-local row
         const int nl = wrow_b + 32 * pr + 8 * lk;  // tile-local first column
-        // the other slices' sums first, then this slice's accumulators (the
-        // accumulators are read at their point of use, which keeps the
-        // compiler from moving them out of their registers early)
+        // (the accumulators are read at their point of use, behind a
+        // scheduling barrier, through one vector add each: stored straight
+        // from the accumulator registers, or read any earlier, they make the
+        // compiler rotate the K loop's accumulators through temporaries.
+        // Adding +0 turns a -0 sum into +0, which no later addition can tell
+        // apart.)
         __builtin_amdgcn_sched_barrier(0);
-        float add[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) add[j] = 0.f;
-        const float* a = addend + ml * 256 + nl;
-        for (int s2 = 0; s2 < nadd; ++s2, a += astride) {
-          const f32x4 x0 = reinterpret_cast<const f32x4*>(a)[0];
-          const f32x4 x1 = reinterpret_cast<const f32x4*>(a)[1];
-          add[0] += x0[0]; add[1] += x0[1]; add[2] += x0[2]; add[3] += x0[3];
-          add[4] += x1[0]; add[5] += x1[1]; add[6] += x1[2]; add[7] += x1[3];
-        }
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[fm][2 * pr + (j >> 2)][j & 3] + add[j];
-        if (ml < mlim) {
-          const int64_t e = (int64_t)ml * ldo + nl;
-          if (o_f32) {
-            float* o = reinterpret_cast<float*>(obase) + e;
-            if (vec_ok && nl + 8 <= nlim) {
-              reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
-              reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
-            } else {
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                if (nl + j < nlim) o[j] = v[j];
-            }
-          } else {
-            uint16_t* o = reinterpret_cast<uint16_t*>(obase) + e;
-            if (vec_ok && nl + 8 <= nlim) {
-              u32x4 w;
-              w[0] = pack_bf16x2(v[0], v[1]);
-              w[1] = pack_bf16x2(v[2], v[3]);
-              w[2] = pack_bf16x2(v[4], v[5]);
-              w[3] = pack_bf16x2(v[6], v[7]);
-              *reinterpret_cast<u32x4*>(o) = w;
-            } else {
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                if (nl + j < nlim) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
-            }
-          }
-        }
+        for (int j = 0; j < 8; ++j) v[j] = acc[fm][2 * pr + (j >> 2)][j & 3] + 0.0f;
+        float* o = slot + ml * 256 + nl;
+        reinterpret_cast<f32x4*>(o)[0] = f32x4{v[0], v[1], v[2], v[3]};
+        reinterpret_cast<f32x4*>(o)[1] = f32x4{v[4], v[5], v[6], v[7]};
       }
     }
   };
@@ -662,38 +624,11 @@ gemm_nt_slab(GemmParams p) {
       super_step(k0_of(lks));
     }
     if constexpr (SPLITK) {
-      // A piece that does not start the tile leaves its raw tile in this
-      // workgroup's slot and raises its flag; the owner (the piece with
-      // chunk 0) waits (bounded) for the flags of the workgroups after it
-      // that hold the rest of the tile, and adds their slots in k order.
-      // Release/acquire fences at device scope make the slots written on one
-      // XCD visible on another.
-      // (Chunk-major: the partners are workgroups wg + T, wg + 2T, ...)
+      // slot of this piece: chunk-major, the workgroup's one chunk; stream-K,
+      // piece tile_i (0 or 1) of the workgroup's range
       constexpr int64_t kSlot = 256 * 256;
-      const bool partial = h_kbeg != 0;
-      const int nadd = partial ? 0
-                       : sk_cmaj ? SKN - 1
-                                 : __builtin_amdgcn_readfirstlane(((h_tile + 1) * SKN - 1) / p.sk_items) - wg;
-      const int cstep = sk_cmaj ? p.num_tiles : 1;
-      if (!partial && tid == 0) {
-        for (int i2 = 1; i2 <= nadd; ++i2) {
-          const uint32_t* f = p.sk_flag + wg + i2 * cstep;
-          for (int spin = 0; spin < (1 << 22); ++spin) {
-            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.sk_epoch) break;
-            __builtin_amdgcn_s_sleep(8);
-          }
-        }
-      }
-      __builtin_amdgcn_s_barrier();
-      if (!partial) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      int tm, tn;
-      tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-      epilogue_sk(partial, p.sk_part + (int64_t)wg * kSlot, tm * BM, tn * OUT_BN,
-                  p.sk_part + (int64_t)(wg + cstep) * kSlot, nadd, (int64_t)cstep * kSlot);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __builtin_amdgcn_s_barrier();
-      if (partial && tid == 0)
-        __hip_atomic_store(p.sk_flag + wg, p.sk_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int slot = sk_cmaj ? wg : 2 * wg + tile_i;
+      epilogue_part(p.sk_part + (int64_t)slot * kSlot);
       continue;
     }
 
@@ -716,6 +651,73 @@ gemm_nt_slab(GemmParams p) {
       }
     } else {
       epilogue(m0, n0, p.out_f32 != 0, act_on, T{}, F{});
+    }
+  }
+}
+
+// Second launch of a split-K product: out = the sum of the pieces' partial
+// tiles, in k order, rounded once to the output type.  Block b covers rows
+// 8 (b % 32) .. + 8 of tile b / 32; thread t covers 8 consecutive columns of
+// one of those rows.  Chunk-major: the pieces of tile t are the slots
+// j T + t, j = 0 .. n - 1.  Stream-K: chunk range [w q, (w + 1) q) of
+// workgroup w covers the tail of one tile and/or the head of the next; its
+// piece i lives in slot 2 w + i, and the workgroups covering tile t are
+// t n / q .. ((t + 1) n - 1) / q.
+__global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
+  const int t = blockIdx.x >> 5;
+  const int r = ((blockIdx.x & 31) << 3) + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) << 3;
+  int tm, tn;
+  tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+  const int m = tm * 256 + r, n = tn * 256 + c;
+  if (t >= p.num_tiles || m >= p.M || n >= p.N) return;
+  int s0, s1, sstep;  // slots s0, s0 + sstep, ..., up to s1 inclusive (workgroup-indexed for stream-K)
+  if (p.items == 0) {
+    s0 = t;
+    s1 = t + (p.chunks - 1) * p.num_tiles;
+    sstep = p.num_tiles;
+  } else {
+    s0 = (t * p.chunks) / p.items;
+    s1 = ((t + 1) * p.chunks - 1) / p.items;
+    sstep = 1;
+  }
+  float v[8];
+  for (int w = s0; w <= s1; w += sstep) {
+    const int slot = p.items == 0 ? w : 2 * w + (t - (w * p.items) / p.chunks);
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)slot * (256 * 256) + r * 256 + c);
+    const f32x4 x0 = src[0], x1 = src[1];
+    if (w == s0) {
+      v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
+      v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
+    } else {
+      v[0] += x0[0]; v[1] += x0[1]; v[2] += x0[2]; v[3] += x0[3];
+      v[4] += x1[0]; v[5] += x1[1]; v[6] += x1[2]; v[7] += x1[3];
+    }
+  }
+  const bool vec = p.out_vec && n + 8 <= p.N;
+  if (p.out_f32) {
+    float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * p.N + n;
+    if (vec) {
+      __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(o));
+      __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(o) + 1);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < p.N) o[j] = v[j];
+    }
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m * p.N + n;
+    if (vec) {
+      u32x4 w;
+      w[0] = pack_bf16x2(v[0], v[1]);
+      w[1] = pack_bf16x2(v[2], v[3]);
+      w[2] = pack_bf16x2(v[4], v[5]);
+      w[3] = pack_bf16x2(v[6], v[7]);
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < p.N) o[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
     }
   }
 }

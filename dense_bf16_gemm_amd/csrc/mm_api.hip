@@ -366,16 +366,13 @@ struct Plan {
 // their persistent scheduler (PR "Implement persistent matmul scheduling",
 // review notes).  Here: when a K-contiguous single-weight product has fewer
 // 256 x 256 tiles than the grid has workgroups, each tile's K loop is cut into
-// n chunks and the tiles * n chunks are dealt to the resident workgroups in
-// equal contiguous ranges (stream-K); the partial tiles meet in a
-// caller-provided workspace.
+// n chunks and the tiles * n chunks are dealt to the resident workgroups
+// (one chunk each, or equal contiguous ranges: stream-K); every piece leaves
+// its fp32 partial tile in a caller-provided workspace, and a second launch
+// (splitk_reduce) adds them in k order.
 // ----------------------------------------------------------------------------
 constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
-// The flags always occupy the first 4 KiB of a workspace (one per workgroup,
-// at most 1024), so that a later call of another shape never reads a flag
-// from bytes an earlier call used for partial tiles.
-constexpr int64_t kSkFlagBytes = 4096;
-constexpr int64_t kSkMaxWgs = kSkFlagBytes / 4;
+constexpr int64_t kSkMaxWgs = 1024;  // bounds the workspace (at most 512 MiB)
 
 // plain K-contiguous products (no bias or activation: the pieces' sums meet
 // before any epilogue math would apply)
@@ -432,19 +429,21 @@ SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
   return sp;
 }
 
+// one slot per chunk-major workgroup; two per stream-K workgroup (its range
+// may end one tile and start the next)
 int64_t splitk_ws_bytes(const SkPlan& sp) {
   if (sp.n <= 1) return 0;
-  return kSkFlagBytes + sp.wgs * kSkSlotBytes;
+  return (sp.q == 0 ? 1 : 2) * sp.wgs * kSkSlotBytes;
 }
 
-// Work units of a stream-K launch run on this many workgroups, all resident
-// at once (an owner waits for the workgroups after it).
+// Work units of a split-K launch are dealt to this many workgroups: one wave
+// of resident workgroups (no workgroup waits for another, so residency is a
+// matter of speed only).
 int64_t splitk_wgs(const Config& c, int cus, int occ) {
   const int64_t resident = (int64_t)cus * occ;
   return c.grid > 0 && c.grid < resident ? c.grid : resident;
 }
 
-std::atomic<uint32_t> g_sk_epoch{0};
 
 // Everything but the device-dependent grid size; no HIP calls.
 mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan& sp = SkPlan()) {
@@ -524,8 +523,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     p.k_alt = 0;
     p.sk_chunks = sp.n;
     p.sk_items = sp.q;
-    p.sk_flag = static_cast<uint32_t*>(r.ws);
-    p.sk_part = reinterpret_cast<float*>(static_cast<char*>(r.ws) + kSkFlagBytes);
+    p.sk_part = static_cast<float*>(r.ws);
   }
   pl->kernel = k;
   pl->threads = k->wgm * k->wgn * 64;  // the selected kernel's block size
@@ -555,9 +553,6 @@ mm_status run(const Request& r, void* stream) {
         return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
       if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
       if ((s = plan_host(r, c, &pl, sp)) != MM_OK) return s;
-      uint32_t e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-      if (e == 0) e = g_sk_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-      pl.p.sk_epoch = e;
     }
   }
   if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
@@ -574,6 +569,27 @@ mm_status run(const Request& r, void* stream) {
   hipError_t e = hipLaunchKernel(pl.kernel->fn, dim3((unsigned)grid), dim3(pl.threads), args, 0,
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel: ") + hipGetErrorString(e));
+  if (sp.n > 1) {
+    // the pieces' partial tiles meet: 32 blocks of 8 rows per tile
+    mmk::SkReduceParams rp;
+    rp.part = pl.p.sk_part;
+    rp.out = r.out;
+    rp.M = (int)r.M;
+    rp.N = (int)r.N;
+    rp.tiles_m = pl.p.tiles_m;
+    rp.tiles_n = pl.p.tiles_n;
+    rp.num_tiles = pl.p.num_tiles;
+    rp.group_m = pl.p.group_m;
+    rp.chunks = sp.n;
+    rp.items = sp.q;
+    rp.out_f32 = pl.p.out_f32;
+    rp.out_vec = pl.p.out_vec;
+    void* rargs[] = {&rp};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::splitk_reduce), dim3((unsigned)(32 * rp.num_tiles)),
+                        dim3(256), rargs, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(MM_ERR_HIP, std::string("hipLaunchKernel (split-K reduction): ") + hipGetErrorString(e));
+  }
   return MM_OK;
 }
 

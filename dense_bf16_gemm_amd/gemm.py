@@ -39,9 +39,9 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-# One zero-filled split-K workspace per device, grown on demand.  Calls on one
-# stream may share it (each launch stamps it with a fresh number); calls in
-# flight on different streams at once must pass their own.
+# One split-K workspace per device, grown on demand.  Calls on one stream may
+# share it (a call reads only slots it has written itself, in stream order);
+# calls in flight on different streams at once must pass their own.
 _workspaces: dict = {}
 
 
@@ -49,7 +49,7 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -77,7 +77,7 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype = torch.bflo
     """MatmulOp form: out = A @ B with A [M,K] and B [K,N] (either may be a
     transposed view), fp32 accumulation, bf16 or fp32 output.  `workspace`
     enables split-K for shapes with too few output tiles (see
-    mm_workspace_size): "auto", None (off) or a zero-filled uint8 tensor."""
+    mm_workspace_size): "auto", None (off) or a uint8 tensor."""
     _check(A, "A")
     _check(B, "B")
     M, K = A.shape

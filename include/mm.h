@@ -152,17 +152,17 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * (MM_NT) product -- mm_matmul, or mm_linear with MM_EPI_NONE -- with K a
  * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
  * workgroups, the _ws entry points below cut each tile's K loop into chunks
- * and deal the chunks of all tiles to the resident workgroups in equal
- * contiguous ranges (stream-K); the fp32 partial tiles meet in this workspace
- * (4 KiB of flags, then one 256 KiB slot per workgroup).
+ * and deal the chunks of all tiles to the resident workgroups (one chunk
+ * each, or equal contiguous ranges: stream-K); each piece leaves its fp32
+ * partial tile in this workspace (one 256 KiB slot per workgroup, two per
+ * stream-K workgroup), and a second kernel on the same stream adds them.
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
  *   bytes   receives the size a call of this shape on the current device may
  *           use; 0 = the shape runs without one.  Queries the device (CU
  *           count, occupancy); launches nothing.
- * Workspace contract: device memory, 256-byte aligned, zero-filled before its
- * first use, reusable by later calls on the same stream; two calls in flight
- * at once must not share it, and a captured graph must not replay a call that
- * uses one (each call stamps it with a fresh launch number).               */
+ * Workspace contract: device memory, 256-byte aligned, any contents (every
+ * byte a call reads it has written first), reusable by later calls on the
+ * same stream; two calls in flight at once must not share it.             */
 mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
                             int64_t* bytes);
 
@@ -170,9 +170,9 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
  * workspace, or a shape that needs none, they behave exactly as mm_matmul /
  * mm_linear.  A workspace smaller than reported returns MM_ERR_INVALID_VALUE;
  * one that overlaps an operand or the output returns MM_ERR_INVALID_VALUE.
- * Still one kernel per call; a tile's partial sums are added in k order, so
- * results are reproducible run to run (they differ from the unsplit
- * kernel's by fp32 rounding order only).                                   */
+ * A split call enqueues two kernels (the pieces, then their sum); a tile's
+ * partial sums are added in k order, so results are reproducible run to run
+ * (they differ from the unsplit kernel's by fp32 rounding order only).     */
 mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
                        mm_layout layout, mm_out_dtype out_dtype, void* workspace,
                        int64_t workspace_bytes, void* stream);

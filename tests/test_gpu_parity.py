@@ -347,12 +347,13 @@ def test_splitk_mapping_bitexact(dev, case, out_f32):
         nbytes = binding.workspace_size("matmul", M, N, K)
         say("split-K mapping", (M, N, K), cfg, "f32" if out_f32 else "bf16", nbytes)
         assert nbytes > 0, "this shape should take the split-K path"
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        # stale contents must not matter: the workspace starts as NaN bytes
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
         A, B = synth.dense_int_operands(M, N, K, "nt", seed=M + 3 * N + K)
         A, B = A.to(dev), B.to(dev)
         ref, bits = oracle.gemm(synth.bits(A.cpu()), synth.bits(B.cpu()), "nt")
         out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
-        for rep in range(3):  # the same workspace again: fresh launch numbers each time
+        for rep in range(3):  # the same workspace again
             out.fill_(float("nan"))
             call_matmul_ws(A, B, M, N, K, out_f32, out, ws, nbytes)
             torch.cuda.synchronize()
@@ -367,8 +368,8 @@ def test_splitk_mapping_bitexact(dev, case, out_f32):
 def test_splitk_workspace_shared_across_shapes(dev):
     """One workspace, calls of two shapes with different workgroup counts and
     dealings alternating (chunk-major 16 chunks on 6 tiles; stream-K ranges on
-    4 tiles): each call's flags sit where the other's never put partial tiles,
-    so every result keeps the oracle's bits."""
+    4 tiles): each call reads only the slots it has just written, so every
+    result keeps the oracle's bits."""
     cases = [(520, 395, 8192, None), (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")]
     sizes = []
     for (M, N, K, cfg) in cases:
