@@ -182,11 +182,16 @@ def main() -> int:
     tiles = binding.describe_config(w.form, w.M, w.N, w.K, w.layout)
     cfg = dict(kv.split("=") for kv in tiles.split(","))
     ffn = str(w.form == "ffn").lower()
-    if cfg["KERNEL"] == "gemm_nt_slab":  # <tile, waves, FFN, split-K, pre-activation output>
-        splitk = (w.form != "ffn" and w.epilogue == "none"
-                  and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
+    # the workspace the step passes ("auto") turns under-filled plain products
+    # into split-K: the slab kernel's split-K instance, then splitk_reduce
+    splitk = (w.form != "ffn" and w.epilogue == "none"
+              and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
+    if splitk:
+        kernel = "mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false> + mmk::splitk_reduce"
+        tiles = "BM=256,BN=256,WM=2,WN=2,SPLITK,KERNEL=gemm_nt_slab+splitk_reduce"
+    elif cfg["KERNEL"] == "gemm_nt_slab":  # <tile, waves, FFN, split-K, pre-activation output>
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
-                  f"{str(splitk).lower()}, false>")
+                  f"false, false>")
     elif cfg["KERNEL"] == "gemm_ws":
         kernel = "mmk::gemm_ws"
     else:
