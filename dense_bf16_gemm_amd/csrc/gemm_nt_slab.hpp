@@ -657,21 +657,17 @@ gemm_nt_slab(GemmParams p) {
 
 // Second launch of a split-K product: out = the sum of the pieces' partial
 // tiles, in k order, rounded once to the output type.  Block b covers rows
-// 8 (b % 32) .. + 8 of tile b / 32; thread t covers 8 consecutive columns of
-// one of those rows.  Chunk-major: the pieces of tile t are the slots
-// j T + t, j = 0 .. n - 1.  Stream-K: chunk range [w q, (w + 1) q) of
+// 8 (b % 32) .. + 8 of tile b / 32.  Chunk-major: the pieces of tile t are the
+// slots j T + t, j = 0 .. n - 1.  Stream-K: chunk range [w q, (w + 1) q) of
 // workgroup w covers the tail of one tile and/or the head of the next; its
 // piece i lives in slot 2 w + i, and the workgroups covering tile t are
 // t n / q .. ((t + 1) n - 1) / q.
 __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
   const int t = blockIdx.x >> 5;
-  const int r = ((blockIdx.x & 31) << 3) + (threadIdx.x >> 5);
-  const int c = (threadIdx.x & 31) << 3;
+  const int r0 = (blockIdx.x & 31) << 3;
   int tm, tn;
   tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-  const int m = tm * 256 + r, n = tn * 256 + c;
-  if (t >= p.num_tiles || m >= p.M || n >= p.N) return;
-  int s0, s1, sstep;  // slots s0, s0 + sstep, ..., up to s1 inclusive (workgroup-indexed for stream-K)
+  int s0, s1, sstep;  // workgroups (stream-K) or slots (chunk-major) s0, s0 + sstep, .., s1
   if (p.items == 0) {
     s0 = t;
     s1 = t + (p.chunks - 1) * p.num_tiles;
@@ -681,10 +677,42 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
     s1 = ((t + 1) * p.chunks - 1) / p.items;
     sstep = 1;
   }
+  auto slot_of = [&](int w) { return p.items == 0 ? w : 2 * w + (t - (w * p.items) / p.chunks); };
+  if (!p.out_vec) {
+    // rows not 16-byte aligned: thread = one column of the 8 rows, so that
+    // each load and each store of a wave covers consecutive elements
+    const int c = threadIdx.x;
+    const int n = tn * 256 + c;
+    if (n >= p.N) return;
+    float v[8];
+    for (int w = s0; w <= s1; w += sstep) {
+      const float* src = p.part + (int64_t)slot_of(w) * (256 * 256) + r0 * 256 + c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = src[j * 256];
+        v[j] = w == s0 ? x : v[j] + x;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = tm * 256 + r0 + j;
+      if (m >= p.M) break;
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[(int64_t)m * p.N + n] = v[j];
+      else
+        reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] =
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));
+    }
+    return;
+  }
+  // aligned rows: thread = 8 consecutive columns of one row, 16-byte accesses
+  const int r = r0 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) << 3;
+  const int m = tm * 256 + r, n = tn * 256 + c;
+  if (m >= p.M || n >= p.N) return;
   float v[8];
   for (int w = s0; w <= s1; w += sstep) {
-    const int slot = p.items == 0 ? w : 2 * w + (t - (w * p.items) / p.chunks);
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)slot * (256 * 256) + r * 256 + c);
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)slot_of(w) * (256 * 256) + r * 256 + c);
     const f32x4 x0 = src[0], x1 = src[1];
     if (w == s0) {
       v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
@@ -694,7 +722,7 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
       v[4] += x1[0]; v[5] += x1[1]; v[6] += x1[2]; v[7] += x1[3];
     }
   }
-  const bool vec = p.out_vec && n + 8 <= p.N;
+  const bool vec = n + 8 <= p.N;
   if (p.out_f32) {
     float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * p.N + n;
     if (vec) {
