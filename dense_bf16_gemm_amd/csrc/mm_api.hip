@@ -128,6 +128,7 @@ struct Config {
   int pipe = 3;   // preferred kernel family: 4 wave-specialized (BN=128, WN=4), 3 slab ring,
                   // 2 ping-pong, 1 pipeline, 0 basic
   int sk = 0;     // split-K slices when a workspace is given: 0 automatic, 1 off, n forced
+  bool forced = false;  // set by mm_set_config / MM_FORCE_CONFIG (not by the heuristic)
 };
 
 std::mutex g_cfg_mu;
@@ -220,9 +221,32 @@ Config choose_config(bool ffn, int64_t M, int64_t N, int64_t K) {
   read_env_once();
   {
     std::lock_guard<std::mutex> g(g_cfg_mu);
-    if (g_cfg_forced) return g_cfg_force;
+    if (g_cfg_forced) {
+      Config c = g_cfg_force;
+      c.forced = true;
+      return c;
+    }
   }
   return heuristic(ffn, M, N, K);
+}
+
+// Band height that makes each XCD's share of a launch the most compact block
+// of tiles: an XCD runs `per` consecutive tiles of the band order, which with
+// band height g form a g x per/g block whose panels number g + per/g (the
+// smallest such g).  2047 x 3001 x 65536 split in 2 (96 tiles of 8 x 12, 24
+// workgroups per XCD): g = 4 gives 4 x 6 blocks (10 panels) instead of 8 x 3
+// (11 panels): 644.3 -> 633.0 us per call (same-box A/B, three alternations).
+int compact_band(int64_t per, int64_t tiles_m) {
+  int best = 1;
+  int64_t cost = INT64_MAX;
+  for (int g = 1; g <= tiles_m && g <= 64; ++g) {
+    const int64_t c = g + cdiv(per, g);
+    if (c < cost) {
+      cost = c;
+      best = g;
+    }
+  }
+  return best;
 }
 
 // K-direction alternation pays off once one tile's K panels no longer stay
@@ -552,7 +576,10 @@ mm_status run(const Request& r, void* stream) {
       if (r.ws_bytes < splitk_ws_bytes(sp))
         return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
       if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-      if ((s = plan_host(r, c, &pl, sp)) != MM_OK) return s;
+      // the split launch's own tile order (a forced configuration keeps its G)
+      Config cs = c;
+      if (!c.forced) cs.group = compact_band(cdiv(sp.wgs, mmk::kNumXcd), cdiv(r.M, 256));
+      if ((s = plan_host(r, cs, &pl, sp)) != MM_OK) return s;
     }
   }
   if ((s = kernel_occupancy(pl.kernel, &occ)) != MM_OK) return s;
@@ -563,7 +590,7 @@ mm_status run(const Request& r, void* stream) {
   if (std::getenv("MM_LOG"))
     std::fprintf(stderr, "libmm: M=%lld N=%lld K=%lld layout=%d ffn=%d -> BM=%d BN=%d WM=%d WN=%d G=%d "
                  "XCD=%d KALT=%d grid=%lld tiles=%d chunks=%d\n", (long long)r.M, (long long)r.N,
-                 (long long)r.K, r.layout, (int)r.ffn, c.bm, c.bn, c.wgm, c.wgn, c.group, c.xcd,
+                 (long long)r.K, r.layout, (int)r.ffn, c.bm, c.bn, c.wgm, c.wgn, pl.p.group_m, c.xcd,
                  pl.p.k_alt, (long long)grid, pl.p.num_tiles, pl.p.sk_chunks);
   void* args[] = {&pl.p};
   hipError_t e = hipLaunchKernel(pl.kernel->fn, dim3((unsigned)grid), dim3(pl.threads), args, 0,
