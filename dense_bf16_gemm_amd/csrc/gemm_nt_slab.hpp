@@ -125,14 +125,36 @@ __device__ __forceinline__ void spread_loop_latch() {
   __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read of 16-bit elements (gfx950).  Within each group of 16
+// lanes, lane 4r + q supplies the address of 4 consecutive elements (row r,
+// column block q of a 4 x 16 block) and lane i receives column i of the 4
+// rows: element e is row e's element i.  The restrict parameter gives the
+// read alias information: without it the compiler treats the intrinsic as
+// possibly reading what any direct-to-LDS copy in flight writes and waits
+// for all of them (vmcnt 0) before it, as it does not for plain LDS loads;
+// the copies and these reads are ordered by the kernel's own waits and
+// barriers.
+__device__ __forceinline__ s16x4 lds_read_tr16(__attribute__((address_space(3))) char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
 // SiLU as g / (1 + 2^(-g log2 e)).
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950409f));
 }
 
-template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false>
+template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false,
+          bool BKN = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
+  // BKN: the weight operand is stored [K][N] (the MatmulOp form's B as
+  // given, N contiguous).  Its slab of a super-step is 64 k-rows of 256
+  // columns (512 bytes), copied as stored, and the fragments are read with
+  // the LDS transpose read, which hands each lane 4 consecutive k of one
+  // column: two of them make the 8 k of an MFMA operand.
+  static_assert(!(BKN && (FFN || SPLITK || PRE)), "[K][N] weights in the single-weight form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
@@ -187,6 +209,15 @@ gemm_nt_slab(GemmParams p) {
   const uint32_t row_bytes = (uint32_t)ld * 2u;
   const uint32_t lane_base = (uint32_t)crow * row_bytes + 16u * (uint32_t)cchunk;
   constexpr int kRsrcWord3 = 0x00020000;
+  // [K][N] weight slab: copy c of this wave fills unit rows 2j, 2j + 1 (k),
+  // j = 4c + wave, 512 bytes each; lane L fills row 2j + L/32, physical
+  // 16-byte chunk L%32, from logical chunk (L%32) ^ (4 (row & 3)).  Row & 3
+  // is 2 (wave & 1) + L/32 for every copy, so the logical chunk is a lane
+  // constant.
+  const uint32_t rowb_kn = (uint32_t)N * 2u;
+  const int kn_row = lane >> 5;
+  const int kn_chunk = (lane & 31) ^ (((2 * (wave & 1) + kn_row) & 3) << 2);
+  const uint32_t lane_kn = (uint32_t)kn_row * rowb_kn + 16u * (uint32_t)kn_chunk;
 
   // Descriptors of the tile the copies currently fetch (cur) and of the
   // workgroup's next tile (nxt; the current one again after the last tile,
@@ -194,6 +225,7 @@ gemm_nt_slab(GemmParams p) {
   struct TileDesc {
     uint64_t a_base, b0_base, b1_base;
     uint32_t a_rec, b_rec;
+    uint64_t b_rem;  // [K][N] weights: bytes from b0_base to the end of B
     int alt;
     int kbeg;  // first super-step of a split-K slice (0 otherwise)
   };
@@ -244,8 +276,11 @@ gemm_nt_slab(GemmParams p) {
     d.a_base = reinterpret_cast<uint64_t>(p.A + ea + (int64_t)m0 * ld);
     d.a_rec = (uint32_t)mrows * row_bytes;
     d.b_rec = (uint32_t)nrows * row_bytes;
-    d.b0_base = reinterpret_cast<uint64_t>(p.B + eb + (int64_t)n0 * ld);
+    d.b0_base = reinterpret_cast<uint64_t>(p.B + eb + (BKN ? (int64_t)n0 : (int64_t)n0 * ld));
     d.b1_base = FFN ? reinterpret_cast<uint64_t>(p.B2 + eb + (int64_t)n0 * ld) : d.b0_base;
+    // columns past N read the next row's values (or zeros past the end of
+    // B): they only reach output columns past N, which are never stored
+    d.b_rem = BKN ? ((uint64_t)K * (uint64_t)N - (uint64_t)n0) * 2u : 0;
     d.alt = SPLITK ? 0 : (p.k_alt && (tile_i & 1));
     d.kbeg = kbeg;
     return d;
@@ -300,6 +335,17 @@ gemm_nt_slab(GemmParams p) {
         lane_base + (uint32_t)(8 * (c * NW + wave)) * row_bytes, 0, 0, 0);
   };
   auto copy_b = [&](int c, uint32_t kbytes, int unit) __attribute__((always_inline)) {
+    if constexpr (BKN) {
+      // the super-step's k rows: the base moves by k0 rows of N columns
+      const uint64_t kb = (uint64_t)(kbytes >> 1) * rowb_kn;
+      const uint64_t rem = cur.b_rem - kb;
+      const uint32_t rec = rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem;
+      const __amdgpu_buffer_rsrc_t r = rsrc(cur.b0_base + kb, rec);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
+          lane_kn + (uint32_t)(2 * (c * NW + wave)) * rowb_kn, 0, 0, 0);
+      return;
+    }
     bool up;
     const int prow = wrow_of(c, &up);
     const __amdgpu_buffer_rsrc_t r = rsrc((up ? cur.b1_base : cur.b0_base) + kbytes, cur.b_rec - kbytes);
@@ -322,8 +368,16 @@ gemm_nt_slab(GemmParams p) {
   const int wrow_a = wave_m * WTM;
   const int wrow_b = wave_n * WTN;
   const uint32_t a_x0 = (uint32_t)((wrow_a + lx) * kSlabRowB + ((lk ^ (lx & 7)) << 4));
-  const uint32_t b_x0 = (uint32_t)((wrow_b + 8 * (lx >> 2) + (lx & 3)) * kSlabRowB +
-                                   ((lk ^ (lx & 3) ^ (((lx >> 3) & 1) << 2)) << 4));
+  const uint32_t b_x0 = BKN
+      // [K][N] slab: lane (lk, lx) of a transpose read supplies k-row
+      // 8 lk + 4 hk + lx / 4 (+ 32 h) and the 4 columns from wrow_b +
+      // 8 (lx & 3) + 4 (fn & 1) + 32 (fn >> 1) (the comb); their 16-byte chunk
+      // 16 wave_n + (lx & 3) + 4 (fn >> 1) sits at chunk ^ 4 (row & 3), i.e.
+      // bits 6..7 of the offset hold (fn >> 1) ^ (lx >> 2): this is the offset
+      // for fn >> 1 = 0, the others XOR 64 (fn >> 1) into it.
+      ? (uint32_t)((8 * lk + (lx >> 2)) * 512 + 256 * wave_n + 16 * (lx & 3) + 64 * (lx >> 2))
+      : (uint32_t)((wrow_b + 8 * (lx >> 2) + (lx & 3)) * kSlabRowB +
+                   ((lk ^ (lx & 3) ^ (((lx >> 3) & 1) << 2)) << 4));
 
   bf16x8 fa[FM];     // activation fragments, refilled row by row
   bf16x8 fb[2][FN];  // weight fragments, double-buffered
@@ -334,6 +388,17 @@ gemm_nt_slab(GemmParams p) {
     fa[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + off));
   };
   auto read_b = [&](int set, int fn, int h, uint32_t ubase) __attribute__((always_inline)) {
+    if constexpr (BKN) {
+      // two transpose reads: k 8 lk + 0..3 and 8 lk + 4..7 of the lane's column
+      typedef __attribute__((address_space(3))) char lds_char;
+      const uint32_t off = (ubase ^ (uint32_t)(64 * (fn >> 1))) + (uint32_t)(32 * h * 512 + 8 * (fn & 1));
+      const s16x4 lo = lds_read_tr16((lds_char*)smem + off);
+      const s16x4 hi = lds_read_tr16((lds_char*)smem + off + 4 * 512);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      fb[set][fn] = __builtin_bit_cast(bf16x8, v);
+      return;
+    }
     const uint32_t off = (((h ^ fn) & 1) ? (ubase ^ 64u) : ubase) +
                          (uint32_t)((4 * (fn & 1) + 32 * (fn >> 1)) * kSlabRowB);
     fb[set][fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + off));
