@@ -146,7 +146,7 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false,
-          bool BKN = false>
+          bool BKN = false, bool AMK = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
   // BKN: the weight operand is stored [K][N] (the MatmulOp form's B as
@@ -155,6 +155,9 @@ gemm_nt_slab(GemmParams p) {
   // the LDS transpose read, which hands each lane 4 consecutive k of one
   // column: two of them make the 8 k of an MFMA operand.
   static_assert(!(BKN && (FFN || SPLITK || PRE)), "[K][N] weights in the single-weight form only");
+  // AMK: the activation operand is stored [K][M] (M contiguous), handled the
+  // same way: 64 k-rows of 256 rows' values per slab, transpose reads.
+  static_assert(!(AMK && (FFN || SPLITK || PRE)), "[K][M] activations in the single-weight form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
@@ -218,6 +221,14 @@ gemm_nt_slab(GemmParams p) {
   const int kn_row = lane >> 5;
   const int kn_chunk = (lane & 31) ^ (((2 * (wave & 1) + kn_row) & 3) << 2);
   const uint32_t lane_kn = (uint32_t)kn_row * rowb_kn + 16u * (uint32_t)kn_chunk;
+  // [K][M] activation slab: the same copy pattern with rows of M values;
+  // lane L fetches logical chunk (L%32) ^ 2 s(row), s(row) = (row & 3) |
+  // 4 (bit 3 of row).  Bit 3 of row 2j + L/32 is bit 0 of the copy index c
+  // (j = 4c + wave), so there are two lane constants, for even and odd c.
+  const uint32_t rowb_km = (uint32_t)M * 2u;
+  const int km_s_lo = (2 * (wave & 1) + kn_row) & 3;
+  const uint32_t lane_km0 = (uint32_t)kn_row * rowb_km + 16u * (uint32_t)((lane & 31) ^ (2 * km_s_lo));
+  const uint32_t lane_km1 = (uint32_t)kn_row * rowb_km + 16u * (uint32_t)((lane & 31) ^ (2 * (km_s_lo | 4)));
 
   // Descriptors of the tile the copies currently fetch (cur) and of the
   // workgroup's next tile (nxt; the current one again after the last tile,
@@ -226,6 +237,7 @@ gemm_nt_slab(GemmParams p) {
     uint64_t a_base, b0_base, b1_base;
     uint32_t a_rec, b_rec;
     uint64_t b_rem;  // [K][N] weights: bytes from b0_base to the end of B
+    uint64_t a_rem;  // [K][M] activations: bytes from a_base to the end of A
     int alt;
     int kbeg;  // first super-step of a split-K slice (0 otherwise)
   };
@@ -273,7 +285,8 @@ gemm_nt_slab(GemmParams p) {
     // batch entry (never with split-K): operand bases move by the strides
     const int64_t ea = SPLITK ? 0 : (int64_t)slice * p.stride_a;
     const int64_t eb = SPLITK ? 0 : (int64_t)slice * p.stride_b;
-    d.a_base = reinterpret_cast<uint64_t>(p.A + ea + (int64_t)m0 * ld);
+    d.a_base = reinterpret_cast<uint64_t>(p.A + ea + (AMK ? (int64_t)m0 : (int64_t)m0 * ld));
+    d.a_rem = AMK ? ((uint64_t)K * (uint64_t)M - (uint64_t)m0) * 2u : 0;
     d.a_rec = (uint32_t)mrows * row_bytes;
     d.b_rec = (uint32_t)nrows * row_bytes;
     d.b0_base = reinterpret_cast<uint64_t>(p.B + eb + (BKN ? (int64_t)n0 : (int64_t)n0 * ld));
@@ -329,6 +342,18 @@ gemm_nt_slab(GemmParams p) {
   // host stub of the kernel uninstantiated, as does deducing the descriptor
   // type.)
   auto copy_a = [&](int c, uint32_t kbytes, int unit) __attribute__((always_inline)) {
+    if constexpr (AMK) {
+      // rows past M read the next k-row's values (or zeros past the end of
+      // A): they only reach output rows past M, which are never stored
+      const uint64_t kb = (uint64_t)(kbytes >> 1) * rowb_km;
+      const uint64_t rem = cur.a_rem - kb;
+      const uint32_t rec = rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem;
+      const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base + kb, rec);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
+          ((c & 1) ? lane_km1 : lane_km0) + (uint32_t)(2 * (c * NW + wave)) * rowb_km, 0, 0, 0);
+      return;
+    }
     const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base + kbytes, cur.a_rec - kbytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
@@ -367,7 +392,15 @@ gemm_nt_slab(GemmParams p) {
   const int lk = lane >> 4;
   const int wrow_a = wave_m * WTM;
   const int wrow_b = wave_n * WTN;
-  const uint32_t a_x0 = (uint32_t)((wrow_a + lx) * kSlabRowB + ((lk ^ (lx & 7)) << 4));
+  const uint32_t a_x0 = AMK
+      // [K][M] slab: lane (lk, lx) of a transpose read supplies k-row
+      // 8 lk + 4 hk + lx / 4 (+ 32 h) and rows wrow_a + 16 fm + 4 (lx & 3) ..
+      // + 3: 16-byte chunk 16 wave_m + 2 fm + (lx & 3) / 2, half (lx & 1), at
+      // chunk ^ 2 s, s = (lx >> 2) | 4 (lk & 1): bits 5..7 of the offset hold
+      // fm ^ s, so this is the offset for fm = 0 and the others XOR 32 fm in
+      ? (uint32_t)((8 * lk + (lx >> 2)) * 512 + 256 * wave_m + 16 * ((lx & 3) >> 1) + 8 * (lx & 1) +
+                   32 * ((lx >> 2) | ((lk & 1) << 2)))
+      : (uint32_t)((wrow_a + lx) * kSlabRowB + ((lk ^ (lx & 7)) << 4));
   const uint32_t b_x0 = BKN
       // [K][N] slab: lane (lk, lx) of a transpose read supplies k-row
       // 8 lk + 4 hk + lx / 4 (+ 32 h) and the 4 columns from wrow_b +
@@ -384,6 +417,15 @@ gemm_nt_slab(GemmParams p) {
   f32x4 acc[FM][FN];
 
   auto read_a = [&](int fm, int h, uint32_t ubase) __attribute__((always_inline)) {
+    if constexpr (AMK) {
+      typedef __attribute__((address_space(3))) char lds_char;
+      const uint32_t off = (ubase ^ (uint32_t)(32 * fm)) + (uint32_t)(32 * h * 512);
+      const s16x4 lo = lds_read_tr16((lds_char*)smem + off);
+      const s16x4 hi = lds_read_tr16((lds_char*)smem + off + 4 * 512);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      fa[fm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      return;
+    }
     const uint32_t off = (((h ^ fm) & 1) ? (ubase ^ 64u) : ubase) + (uint32_t)(16 * fm * kSlabRowB);
     fa[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + off));
   };

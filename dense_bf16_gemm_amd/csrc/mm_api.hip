@@ -74,10 +74,11 @@ struct KernelEntry {
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, true>), {0}, \
    false, true}
 
-// [K][N] weights (MM_NN, and MM_TN's B): the slab kernel with transpose-read fragments
-#define MM_KSKN()                                                                          \
-  {256, 256, 2, 2, true, false, false, 3,                                                  \
-   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, true>), {0}}
+// [K][N] weights and/or [K][M] activations (MM_NN, MM_TN, MM_TT): the slab kernel
+// with transpose-read fragments for the operands stored that way
+#define MM_KSKN(AKC, BKC)                                                                  \
+  {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC)>), {0}}
 
 #define MM_KWS()                                                                           \
   {256, 128, 2, 4, true, true, false, 4, reinterpret_cast<const void*>(&mmk::gemm_ws), {0}}
@@ -87,7 +88,9 @@ struct KernelEntry {
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
 
 KernelEntry g_kernels[] = {
-    MM_KSKN(),
+    MM_KSKN(true, false),
+    MM_KSKN(false, false),
+    MM_KSKN(false, true),
     MM_KSK(),
     MM_KSP(),
     MM_KWS(),
@@ -507,9 +510,10 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     if ((r.batch > 1 || r.out_pre) && (fam == 1 || fam == 2)) continue;
     // the slab kernel runs whole super-steps of 64 k, two of them in flight
     if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
-    // its [K][N]-weight form addresses a super-step's 64 weight rows with
-    // 32-bit buffer offsets
+    // its [K][N]-weight and [K][M]-activation forms address a super-step's
+    // 64 k-rows of such an operand with 32-bit buffer offsets
     if (fam == 3 && !b_kc && (int64_t)mmk::kSlabK * r.N * 2 >= (int64_t(1) << 31)) continue;
+    if (fam == 3 && !a_kc && (int64_t)mmk::kSlabK * r.M * 2 >= (int64_t(1) << 31)) continue;
     k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile

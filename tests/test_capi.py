@@ -115,16 +115,17 @@ def test_config_override_and_rejection(lib):
 def test_heuristic_choices():
     assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=256,BN=256")
     # K-contiguous 256 x 256 tiles run the whole-line slab kernel when K spans two
-    # super-steps of 64, the 32-k pipeline otherwise; [K][N] weights (NN) run the
-    # slab kernel's transpose-read form for whole super-steps; M-contiguous A
-    # (TN, TT) and other NN shapes the basic kernel
+    # super-steps of 64, the 32-k pipeline otherwise; [K][N] weights and [K][M]
+    # activations (NN, TN, TT) run the slab kernel's transpose-read forms for
+    # whole super-steps, the basic kernel for other K
     assert binding.describe_config("linear", 8192, 8192, 8192).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("ffn", 8192, 14336, 4096).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("linear", 8192, 8192, 64).endswith("KERNEL=gemm_nt_pipe")
     assert binding.describe_config("linear", 8192, 8192, 8200).endswith("KERNEL=gemm_nt_pipe")
     assert binding.describe_config("matmul", 8192, 8192, 8192, "nn").endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("matmul", 8192, 8192, 8200, "nn").endswith("KERNEL=gemm_persistent")
-    assert binding.describe_config("matmul", 8192, 8192, 8192, "tn").endswith("KERNEL=gemm_persistent")
+    assert binding.describe_config("matmul", 8192, 8192, 8192, "tn").endswith("KERNEL=gemm_nt_slab")
+    assert binding.describe_config("matmul", 8192, 8192, 8192, "tt").endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("ffn", 8192, 14336, 4096).startswith("BM=256,BN=256")
     small = binding.describe_config("matmul", 256, 256, 256, "nn")
     assert small.startswith("BM=64,BN=64")
