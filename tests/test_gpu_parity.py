@@ -467,6 +467,32 @@ def test_linear_epilogues_random(dev, cfg, epi, K):
     assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
 
 
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("epi", ["bias_gelu_tanh", "none"])
+def test_transposed_storage_random(dev, layout, epi):
+    """Operands stored [K][M] / [K][N] (the slab kernel's transpose-read forms
+    at K a multiple of 64, several tiles, ragged M and N), N(0,1) data, against
+    the oracle within the bf16 and fp32 tolerances."""
+    M, N, K = 520, 392, 512
+    say("transposed storage random", layout, epi, (M, N, K))
+    a_shape = (K, M) if layout in ("tn", "tt") else (M, K)
+    b_shape = (N, K) if layout in ("nt", "tt") else (K, N)
+    A = synth.randn_bf16(a_shape, 1.0, 41)
+    B = synth.randn_bf16(b_shape, K ** -0.5, 42)
+    bias = synth.randn_bf16((N,), 1.0, 43)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    call_linear(A.to(dev), B.to(dev), bias.to(dev) if "bias" in epi else None, M, N, K, layout, epi, out)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(A), synth.bits(B), layout, epi,
+                       bias=synth.bits(bias) if "bias" in epi else None)
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+    out32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    call_matmul(A.to(dev), B.to(dev), M, N, K, layout, True, out32)
+    torch.cuda.synchronize()
+    y32, _ = oracle.gemm(synth.bits(A), synth.bits(B), layout)
+    assert tol_excess(out32.cpu().numpy(), y32, 1e-3) <= 0
+
+
 @pytest.mark.parametrize("cfg", FFN_CONFIGS)
 @pytest.mark.parametrize("K", [264, 256])
 def test_ffn_swiglu_random(dev, cfg, K):
