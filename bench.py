@@ -33,8 +33,9 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 
-# the headers the slab kernel (every benchmarked workload's kernel) is built from
-SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp")
+# the headers the slab kernel (every benchmarked workload's kernel) is built
+# from, and the host code that chooses its tile order and launch
+SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp", "mm_api.hip")
 
 
 def kernel_source_hash() -> str:

@@ -170,8 +170,9 @@ def test_schedule_xcd_locality():
         tiles = [first[b] for b in range(x, 256, 8)]
         rows = {tm for tm, _ in tiles}
         cols = {tn for _, tn in tiles}
-        # 32 workgroups of an XCD cover an 8-row x 4-column block of tiles
-        assert len(rows) == 8 and len(cols) == 4, (x, rows, cols)
+        # 32 workgroups of an XCD cover a 4-row x 8-column block of tiles (band
+        # height 4)
+        assert len(rows) == 4 and len(cols) == 8, (x, rows, cols)
 
 
 def test_batched_argument_checks():
