@@ -666,3 +666,41 @@ def test_int64_operand_offsets(dev):
     del A
     y, _ = oracle.gemm(synth.bits(rows), synth.bits(B), "nt")
     assert tol_excess(out[M - 64:].cpu().numpy(), y, 1e-3) <= 0
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_int64_transposed_storage(dev, layout):
+    """The operand stored [K][M] (tn) or [K][N] (nn) has 65536 x 32776 =
+    2^31 + 524288 elements: the k-row offsets of the transpose-read kernels pass
+    2^32 bytes, and the buffer range is capped.  Checks the 64 outputs nearest
+    the operand's end (last rows for tn, last columns for nn)."""
+    K, big, small = 65536, 32776, 128
+    M, N = (big, small) if layout == "tn" else (small, big)
+    say("int64 transposed storage", layout, (M, N, K))
+    free, _total = torch.cuda.mem_get_info()
+    if free < 14 * 2 ** 30:
+        pytest.skip("needs ~14 GiB of free device memory")
+    g = torch.Generator(device=dev).manual_seed(603)
+    # N(0, 1) activations, N(0, 1/K) weights: outputs of order 1, as in the workloads
+    sigma = 1.0 if layout == "tn" else K ** -0.5
+    Big = torch.randn((K, big), generator=g, device=dev, dtype=torch.float32).mul_(sigma).to(torch.bfloat16)
+    other = synth.randn_bf16((K, small), K ** -0.5, 604)
+    A, B = (Big, other.to(dev)) if layout == "tn" else (other.to(dev), Big)
+    if layout == "nn":  # A [M][K]
+        A = synth.randn_bf16((M, K), 1.0, 605).to(dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # the 256 x 256 slab kernel (the heuristic would take 128 x 128 tiles here)
+    binding.set_config("BM=256,BN=256,WM=2,WN=2,PIPE=3")
+    assert binding.describe_config("matmul", M, N, K, layout).endswith("KERNEL=gemm_nt_slab")
+    call_matmul(A, B, M, N, K, layout, True, out)
+    torch.cuda.synchronize()
+    tail = Big[:, big - 64:].contiguous().cpu()
+    del Big, A, B
+    if layout == "tn":
+        y, _ = oracle.gemm(synth.bits(tail), synth.bits(other), "tn")
+        got = out[M - 64:].cpu().numpy()
+    else:
+        Ah = synth.randn_bf16((M, K), 1.0, 605)
+        y, _ = oracle.gemm(synth.bits(Ah), synth.bits(tail), "nn")
+        got = out[:, N - 64:].cpu().numpy()
+    assert tol_excess(got, y, 1e-3) <= 0
