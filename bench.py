@@ -177,6 +177,7 @@ def main() -> int:
     ms_per_step = ms_total / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     mean_launch = statistics.fmean(per_launch)
+    deciles = statistics.quantiles(per_launch, n=10) if len(per_launch) > 1 else per_launch * 9
     achieved = w.flops / (mean_launch * 1e-3) / 1e12
 
     traffic = traffic_from_profile(name)
@@ -223,6 +224,9 @@ def main() -> int:
             "out_dtype": w.out_dtype,
             "tiles": tiles,
             "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "device": torch.cuda.get_device_name(dev),
+            "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+            "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
         },
         "roofline": {
             "bound": "mfma",
@@ -235,6 +239,8 @@ def main() -> int:
             "launch_ms_mean": round(mean_launch, 5),
             "launch_ms_median": round(statistics.median(per_launch), 5),
             "launch_ms_min": round(min(per_launch), 5),
+            "launch_ms_p10": round(deciles[0], 5),
+            "launch_ms_p90": round(deciles[-1], 5),
         },
         "cpu_baseline": None,
     }
