@@ -1,5 +1,9 @@
-// gemm_nt_slab.hpp -- K-contiguous ("NT") GEMM whose global->LDS copies move
-// whole 128-byte lines, for 256 x 256 tiles on four waves.
+// gemm_nt_slab.hpp -- GEMM whose global->LDS copies move whole lines, for
+// 256 x 256 tiles on four waves.  K-contiguous operands ("NT") are copied as
+// rows of 128 bytes (64 k); an operand stored [K][N] or [K][M] (the BKN and
+// AMK instances: the NN, TN and TT layouts) as k-rows of 512 bytes, read
+// back with the LDS transpose read (see lds_read_tr16 and the BKN/AMK notes
+// in the kernel).
 //
 // Same persistent schedule, tile order and result as gemm_nt_pipe, with
 // three changes aimed at keeping one wave per SIMD issuing MFMAs:
@@ -24,7 +28,8 @@
 //     that tile's first slabs (so they land while this tile's epilogue runs:
 //     section "Syncing persistent matmuls").
 // The host uses this kernel only when K is a multiple of the 64-k super-step
-// and spans at least two of them (ragged K runs gemm_nt_pipe).
+// and spans at least two of them (ragged K runs gemm_nt_pipe, or for the
+// other layouts gemm_persistent).
 #pragma once
 
 #include "gemm_nt_pipe.hpp"
@@ -154,10 +159,10 @@ gemm_nt_slab(GemmParams p) {
   // columns (512 bytes), copied as stored, and the fragments are read with
   // the LDS transpose read, which hands each lane 4 consecutive k of one
   // column: two of them make the 8 k of an MFMA operand.
-  static_assert(!(BKN && (FFN || SPLITK || PRE)), "[K][N] weights in the single-weight form only");
+  static_assert(!(BKN && (FFN || PRE)), "[K][N] weights in the single-weight form only");
   // AMK: the activation operand is stored [K][M] (M contiguous), handled the
   // same way: 64 k-rows of 256 rows' values per slab, transpose reads.
-  static_assert(!(AMK && (FFN || SPLITK || PRE)), "[K][M] activations in the single-weight form only");
+  static_assert(!(AMK && (FFN || PRE)), "[K][M] activations in the single-weight form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one

@@ -65,9 +65,11 @@ struct KernelEntry {
   {256, 256, 2, 2, true, true, FFN, 3,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, FFN>), {0}}
 
-#define MM_KSK()                                                                           \
-  {256, 256, 2, 2, true, true, false, 3,                                                   \
-   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true>), {0}, true}
+// split-K pieces, one instance per operand storage (K-contiguous or not)
+#define MM_KSK(AKC, BKC)                                                                   \
+  {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, !(BKC), !(AKC)>), \
+   {0}, true}
 
 #define MM_KSP()                                                                           \
   {256, 256, 2, 2, true, true, false, 3,                                                   \
@@ -91,7 +93,10 @@ KernelEntry g_kernels[] = {
     MM_KSKN(true, false),
     MM_KSKN(false, false),
     MM_KSKN(false, true),
-    MM_KSK(),
+    MM_KSK(true, true),
+    MM_KSK(true, false),
+    MM_KSK(false, false),
+    MM_KSK(false, true),
     MM_KSP(),
     MM_KWS(),
     MM_KS(false),
@@ -413,11 +418,19 @@ struct Plan {
 constexpr int64_t kSkSlotBytes = 256 * 256 * 4;
 constexpr int64_t kSkMaxWgs = 1024;  // bounds the workspace (at most 512 MiB)
 
-// plain K-contiguous products (no bias or activation: the pieces' sums meet
-// before any epilogue math would apply)
+// whether op(A) / op(B) are stored K-contiguous
+bool a_kcontig(int layout) { return layout == MM_NN || layout == MM_NT; }
+bool b_kcontig(int layout) { return layout == MM_NT || layout == MM_TT; }
+
+// plain products (no bias or activation: the pieces' sums meet before any
+// epilogue math would apply) in the slab kernel's domain: whole super-steps,
+// and 32-bit offsets within a tile's K-contiguous rows and a super-step's
+// k-rows of an operand stored [K][M] / [K][N]
 bool splitk_shape(const Request& r) {
-  return r.batch == 1 && !r.ffn && r.epi == mmk::EPI_NONE && r.layout == MM_NT && r.K % mmk::kSlabK == 0 &&
-         r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31);
+  return r.batch == 1 && !r.ffn && r.epi == mmk::EPI_NONE && r.K % mmk::kSlabK == 0 &&
+         r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31) &&
+         (a_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.M * 2 < (int64_t(1) << 31)) &&
+         (b_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.N * 2 < (int64_t(1) << 31));
 }
 
 struct SkPlan {
@@ -495,7 +508,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   if (sk) {
     c.bm = c.bn = 256;
     c.wgm = c.wgn = 2;
-    k = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
+    k = find_kernel(256, 256, 2, 2, a_kc, b_kc, false, 3, true);
   }
   // the wave-specialized kernel (a configuration override for comparison)
   // takes single-weight K-contiguous products with whole super-steps; other
@@ -588,7 +601,7 @@ mm_status run(const Request& r, void* stream) {
   if (r.ws && splitk_shape(r) && c.sk != 1) {
     // the split-K kernel's grid: one wave of resident workgroups
     int sk_occ = 0;
-    KernelEntry* sk = find_kernel(256, 256, 2, 2, true, true, false, 3, true);
+    KernelEntry* sk = find_kernel(256, 256, 2, 2, a_kcontig(r.layout), b_kcontig(r.layout), false, 3, true);
     if ((s = kernel_occupancy(sk, &sk_occ)) != MM_OK) return s;
     sp = splitk_plan(r, c, splitk_wgs(c, cus, sk_occ));
     if (sp.n > 1) {
@@ -731,7 +744,8 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
   int cus = 0, occ = 0;
   mm_status s;
   if ((s = device_cus(&cus)) != MM_OK) return s;
-  if ((s = kernel_occupancy(find_kernel(256, 256, 2, 2, true, true, false, 3, true), &occ)) != MM_OK)
+  if ((s = kernel_occupancy(find_kernel(256, 256, 2, 2, a_kcontig(r.layout), b_kcontig(r.layout), false, 3, true),
+                            &occ)) != MM_OK)
     return s;
   *bytes = splitk_ws_bytes(splitk_plan(r, c, splitk_wgs(c, cus, occ)));
   return MM_OK;

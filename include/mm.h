@@ -148,8 +148,8 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
 
 /* Split-K workspace (PR "Implement persistent matmul scheduling", review
  * notes: splitting the K loop over workgroups, split-K and stream-K, named
- * there and left out of the persistent scheduler).  When a plain K-contiguous
- * (MM_NT) product -- mm_matmul, or mm_linear with MM_EPI_NONE -- with K a
+ * there and left out of the persistent scheduler).  When a plain product --
+ * mm_matmul, or mm_linear with MM_EPI_NONE, any layout -- with K a
  * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
  * workgroups, the _ws entry points below cut each tile's K loop into chunks
  * and deal the chunks of all tiles to the resident workgroups (one chunk

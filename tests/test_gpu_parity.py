@@ -365,6 +365,37 @@ def test_splitk_mapping_bitexact(dev, case, out_f32):
         binding.set_config(None)
 
 
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("case", [(520, 392, 8192, None),
+                                  (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
+def test_splitk_mapping_layouts(dev, layout, case):
+    """Split-K (chunk-major, and stream-K ranges across tile boundaries) with
+    operands stored [K][M] / [K][N]: integer operands, the oracle's bits."""
+    M, N, K, cfg = case
+    binding.set_config(cfg)
+    try:
+        nbytes = binding.workspace_size("matmul", M, N, K, layout)
+        say("split-K layouts", layout, (M, N, K), cfg, nbytes)
+        assert nbytes > 0, "this shape should take the split-K path"
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
+        A, B = synth.dense_int_operands(M, N, K, layout, seed=M + 5 * N + K)
+        ref, bits = oracle.gemm(synth.bits(A), synth.bits(B), layout)
+        Ad, Bd = A.to(dev), B.to(dev)  # held for the whole call
+        lib = binding.load()
+        for out_f32 in (True, False):
+            out = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
+            st = lib.mm_matmul_ws(Ad.data_ptr(), Bd.data_ptr(), out.data_ptr(), M, N, K,
+                                  binding.LAYOUTS[layout], 1 if out_f32 else 0, ws.data_ptr(), nbytes, stream())
+            binding.check(st, "mm_matmul_ws")
+            torch.cuda.synchronize()
+            if out_f32:
+                np.testing.assert_array_equal(out.cpu().numpy(), ref)
+            else:
+                np.testing.assert_array_equal(to_bits(out), bits)
+    finally:
+        binding.set_config(None)
+
+
 def test_splitk_workspace_shared_across_shapes(dev):
     """One workspace, calls of two shapes with different workgroup counts and
     dealings alternating (chunk-major 16 chunks on 6 tiles; stream-K ranges on
