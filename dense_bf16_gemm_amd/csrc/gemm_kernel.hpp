@@ -350,7 +350,6 @@ gemm_persistent(GemmParams p) {
   if (wg >= units) return;
   const int my_tiles = (units - wg + G - 1) / G;
   const int KT = p.k_tiles;
-  const int total = my_tiles * KT;
 
   const int M = p.M, N = p.N, K = p.K;
   const int64_t lda = A_KC ? (int64_t)K : (int64_t)M;

@@ -427,7 +427,6 @@ gemm_nt_slab(GemmParams p) {
       const uint32_t off = (ubase ^ (uint32_t)(32 * fm)) + (uint32_t)(32 * h * 512);
       const s16x4 lo = lds_read_tr16((lds_char*)smem + off);
       const s16x4 hi = lds_read_tr16((lds_char*)smem + off + 4 * 512);
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
       fa[fm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       return;
     }

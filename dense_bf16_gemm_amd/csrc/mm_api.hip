@@ -119,7 +119,6 @@ KernelEntry g_kernels[] = {
     MM_K(128, 256, 2, 2, true, true, true),
     MM_K(128, 128, 2, 2, true, true, true),
 };
-constexpr int kNumKernels = sizeof(g_kernels) / sizeof(g_kernels[0]);
 
 KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe,
                          bool splitk = false, bool pre = false) {
