@@ -39,14 +39,18 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-# One split-K workspace per device, grown on demand.  Calls on one stream may
-# share it (a call reads only slots it has written itself, in stream order);
-# calls in flight on different streams at once must pass their own.
+# One split-K workspace per (device, stream), grown on demand.  Calls on one
+# stream share it (a call reads only slots it has written itself, in stream
+# order); each stream has its own, so calls in flight on different streams do
+# not race on it.  The tensor is allocated while its stream is current, so the
+# caching allocator reuses its memory, after it is replaced, only in that
+# stream's order.
 _workspaces: dict = {}
 
 
 def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -55,9 +59,9 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
 
 
 def _resolve_ws(workspace, form: str, M: int, N: int, K: int, layout: str, device):
-    """(pointer, bytes) of the split-K workspace: "auto" uses the per-device
-    one sized by mm_workspace_size, None disables split-K, a uint8 tensor is
-    used as given."""
+    """(pointer, bytes) of the split-K workspace: "auto" uses the current
+    stream's cached one, sized by mm_workspace_size; None disables split-K; a
+    uint8 tensor is used as given."""
     if workspace is None:
         return None, 0
     if isinstance(workspace, str):

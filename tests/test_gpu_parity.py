@@ -427,6 +427,41 @@ def test_splitk_workspace_shared_across_shapes(dev):
             np.testing.assert_array_equal(to_bits(out), bits)
 
 
+def test_splitk_auto_workspace_two_streams(dev):
+    """workspace="auto" keeps one workspace per stream: split-K calls of two
+    shapes in flight on two streams at once, with no synchronisation between
+    the streams, each keep the oracle's bits."""
+    from dense_bf16_gemm_amd import gemm as gemm_mod
+    cases = [(520, 395, 8192), (300, 650, 8192)]
+    for (M, N, K) in cases:
+        assert binding.workspace_size("matmul", M, N, K) > 0, "these shapes should take the split-K path"
+    ops = []
+    for (M, N, K) in cases:
+        A, Bt = synth.dense_int_operands(M, N, K, "nt", seed=11 * M + N + K)
+        _, bits = oracle.gemm(synth.bits(A), synth.bits(Bt), "nt")
+        ops.append((A.to(dev), Bt.to(dev), bits))
+    streams = [torch.cuda.Stream(device=dev) for _ in cases]
+    keys = [(dev.index, s.cuda_stream) for s in streams]
+    outs = [[] for _ in cases]
+    try:
+        for s in streams:  # the operands were written on the current stream
+            s.wait_stream(torch.cuda.current_stream(dev))
+        for rep in range(4):
+            for i, ((M, N, K), (A, Bt, _), s) in enumerate(zip(cases, ops, streams)):
+                say("auto workspace, two streams", rep, i, (M, N, K))
+                with torch.cuda.stream(s):
+                    outs[i].append(mm.matmul(A, Bt.t()))
+        torch.cuda.synchronize()
+        assert set(keys) <= set(gemm_mod._workspaces), "each stream keeps its own workspace"
+        assert len({gemm_mod._workspaces[k].data_ptr() for k in keys}) == len(keys)
+        for (_, _, bits), got in zip(ops, outs):
+            for out in got:
+                np.testing.assert_array_equal(to_bits(out), bits)
+    finally:
+        for k in keys:
+            gemm_mod._workspaces.pop(k, None)
+
+
 def test_splitk_random_and_fallbacks(dev):
     M, N, K = 700, 900, 16384
     x = synth.randn_bf16((M, K), 1.0, 11).to(dev)
