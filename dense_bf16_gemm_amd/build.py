@@ -57,7 +57,8 @@ def build(verbose: bool = False) -> str:
 
 
 def resource_usage(path: str = REMARKS):
-    """Parses the resource remarks into {kernel: {field: int}}."""
+    """Parses the resource remarks into {kernel: {field: int}} (True / False
+    fields, such as "Dynamic Stack", as 1 / 0)."""
     out = {}
     cur = None
     with open(path) as f:
@@ -71,8 +72,9 @@ def resource_usage(path: str = REMARKS):
                 out[cur] = {}
             elif cur is not None and ":" in body:
                 key, val = body.rsplit(":", 1)
+                val = {"True": "1", "False": "0"}.get(val.strip(), val.strip())
                 try:
-                    out[cur][key.strip()] = int(val.strip())
+                    out[cur][key.strip()] = int(val)
                 except ValueError:
                     pass
     return out
