@@ -67,8 +67,9 @@ def cpu_baseline(w, tensors, target_s: float):
     from dense_bf16_gemm_amd import synth
 
     if w.form == "matmul":
+        A = tensors["A"] if "A" in tensors else tensors["At"]
         B = tensors["B"] if "B" in tensors else tensors["Bt"]
-        args = dict(A=synth.bits(tensors["A"]), B=synth.bits(B), layout=w.layout, epilogue="none")
+        args = dict(A=synth.bits(A), B=synth.bits(B), layout=w.layout, epilogue="none")
     elif w.form == "linear":
         args = dict(A=synth.bits(tensors["x"]), B=synth.bits(tensors["W"]), layout="nt",
                     epilogue=w.epilogue, bias=synth.bits(tensors["bias"]))
@@ -141,8 +142,9 @@ def main() -> int:
                       device=dev)
 
     if w.form == "matmul":
+        Aop = t["A"] if "A" in t else t["At"].t()  # transposed views, read in place
         Bop = t["B"] if "B" in t else t["Bt"].t()
-        step = lambda: mm.matmul(t["A"], Bop, out.dtype, out=out)  # noqa: E731
+        step = lambda: mm.matmul(Aop, Bop, out.dtype, out=out)  # noqa: E731
     elif w.form == "linear":
         step = lambda: mm.linear(t["x"], t["W"], t["bias"], w.epilogue, out=out)  # noqa: E731
     else:

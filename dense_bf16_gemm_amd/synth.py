@@ -100,7 +100,9 @@ class Workload:
 
 # The five workloads: a small plain matmul, linear+bias+GELU at two scales, the
 # Llama-FFN horizontal fusion, and a long-K non-tile-divisible matmul whose B is
-# a transposed view.
+# a transposed view.  Then the plain matmul at 8192^3 in each operand storage
+# (A as given or stored [K][M] as "At", B as given or stored [N][K] as "Bt"),
+# for the layout comparison.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -117,6 +119,11 @@ WORKLOADS: Dict[str, Workload] = {
                   TensorSpec("W_up", (14336, 4096), 2.0 ** -6, 403))),
         Workload("matmul_longk_nt_f32_2047x3001x65536", "matmul", 2047, 3001, 65536, "nt", "none", "f32",
                  (TensorSpec("A", (2047, 65536), 1.0, 501), TensorSpec("Bt", (3001, 65536), 2.0 ** -8, 502))),
+    ] + [
+        Workload(f"matmul_{lay}_8192", "matmul", 8192, 8192, 8192, lay, "none", "bf16",
+                 (TensorSpec("At" if lay[0] == "t" else "A", (8192, 8192), 1.0, 601 + 2 * i),
+                  TensorSpec("Bt" if lay[1] == "t" else "B", (8192, 8192), 8192 ** -0.5, 602 + 2 * i)))
+        for i, lay in enumerate(("nn", "nt", "tn", "tt"))
     ]
 }
 

@@ -577,8 +577,8 @@ def test_ffn_swiglu_random(dev, cfg, K):
 def run_workload(w: synth.Workload, t, dev):
     g = {k: v.to(dev) for k, v in t.items()}
     if w.form == "matmul":
-        A = g["A"]
-        B = g["B"] if "B" in g else g["Bt"].t()  # transposed view, read in place
+        A = g["A"] if "A" in g else g["At"].t()  # transposed views, read in place
+        B = g["B"] if "B" in g else g["Bt"].t()
         return mm.matmul(A, B, torch.float32 if w.out_dtype == "f32" else torch.bfloat16)
     if w.form == "linear":
         return mm.linear(g["x"], g["W"], g["bias"], w.epilogue)
@@ -587,8 +587,9 @@ def run_workload(w: synth.Workload, t, dev):
 
 def oracle_args(w: synth.Workload, t):
     if w.form == "matmul":
+        A = t["A"] if "A" in t else t["At"]
         B = t["B"] if "B" in t else t["Bt"]
-        return dict(A=synth.bits(t["A"]), B=synth.bits(B), layout=w.layout, epilogue="none")
+        return dict(A=synth.bits(A), B=synth.bits(B), layout=w.layout, epilogue="none")
     if w.form == "linear":
         return dict(A=synth.bits(t["x"]), B=synth.bits(t["W"]), layout="nt", epilogue=w.epilogue,
                     bias=synth.bits(t["bias"]))
