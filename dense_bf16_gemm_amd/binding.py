@@ -13,6 +13,7 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmm.so")
+FULLSYNC_LIB_PATH = os.path.join(HERE, "libmm_fullsync.so")
 
 MM_OK, MM_ERR_INVALID_VALUE, MM_ERR_UNSUPPORTED, MM_ERR_MISALIGNED, MM_ERR_HIP = range(5)
 LAYOUTS = {"nn": 0, "nt": 1, "tn": 2, "tt": 3}
@@ -39,13 +40,20 @@ class MMError(RuntimeError):
 def load(path: str = LIB_PATH):
     """Loads libmm.so once; raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """Opens one build of the library (libmm.so, or the race-check build
+    libmm_fullsync.so next to it) with its prototypes set; raises if it is
+    missing.  Each build is opened with its own symbol scope."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -m dense_bf16_gemm_amd.build, or __graft_entry__.build())")
-    lib = ctypes.CDLL(path)
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.mm_matmul.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.mm_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
@@ -69,7 +77,6 @@ def load(path: str = LIB_PATH):
     lib.mm_status_string.restype = ctypes.c_char_p
     lib.mm_last_error.argtypes = []
     lib.mm_last_error.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

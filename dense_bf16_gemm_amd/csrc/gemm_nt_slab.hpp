@@ -497,6 +497,14 @@ gemm_nt_slab(GemmParams p) {
     const int cua = next_unit(nub);                        // A slab of q+2
     const int cub = ua;                                    // weight slab of q+2
     const uint32_t a_nxt = a_x0 + (uint32_t)(nua * UNIT), b_nxt = b_x0 + (uint32_t)(nub * UNIT);
+#ifdef MM_DEBUG_FULL_SYNC
+    // Race-check build: every copy landed and every LDS read done, in every
+    // wave, before the super-step starts; its results must equal the normal
+    // build's bit for bit.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#endif
 
     // k-step 2q: MFMAs on half 0; half 1 of q (same units) into fa and fb[1]
 #pragma unroll
@@ -527,7 +535,11 @@ gemm_nt_slab(GemmParams p) {
     // This wave's copies of q+1 have landed (only the A slab of q+2 may still
     // be in flight) and its reads of q's units are done; after the barrier
     // q+1 is visible to all waves and q's units may be overwritten.
+#ifdef MM_DEBUG_FULL_SYNC
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the A slab of q+2 too
+#else
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS));
+#endif
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_a(4, 0, a_nxt);

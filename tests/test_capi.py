@@ -39,6 +39,15 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_race_check_build_loads_and_exports_every_declared_symbol():
+    """The MM_DEBUG_FULL_SYNC build (used only by the GPU race check) is
+    built beside libmm.so and has the same interface."""
+    other = binding.open_library(binding.FULLSYNC_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(other, name), name
+    assert other.mm_status_string(0).decode() == "MM_OK"
+
+
 def test_status_strings(lib):
     for code, name in enumerate(["MM_OK", "MM_ERR_INVALID_VALUE", "MM_ERR_UNSUPPORTED",
                                  "MM_ERR_MISALIGNED", "MM_ERR_HIP"]):

@@ -40,7 +40,6 @@ CONFIGS = [
 ]
 FFN_CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
-    "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     # a small persistent grid: several tiles per workgroup, K direction
     # alternating between them, prefetch running across tile boundaries
     "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",

@@ -1,0 +1,153 @@
+"""Race check: the library built with MM_DEBUG_FULL_SYNC (the slab kernel
+drains every global->LDS copy and waits at a barrier before each super-step)
+against the normal build, bit for bit.
+
+The extra waits change only timing, never the arithmetic or its order, so any
+difference means the normal build reads an LDS unit before its copy landed, or
+overwrites one that a wave still reads.  (The pages trace a wrong result to a
+missing write-after-read synchronisation in the pipelined K loop: PR
+"Translate MmaOp patterns properly on Hopper", commit list.)  The cases cover
+every slab instance: the four operand storages, the FFN fusion, the second
+(pre-activation) output, chunk-major and stream-K split-K, and grids small
+enough that the ring runs on across several tiles per workgroup.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from dense_bf16_gemm_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+SLAB = "BM=256,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3"
+
+
+@pytest.fixture(scope="module")
+def libs():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return binding.load(), binding.open_library(binding.FULLSYNC_LIB_PATH)
+
+
+def say(*a):
+    print("case:", *a, flush=True)
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def assert_slab(libs, cfg, form, M, N, K, layout):
+    """The configuration selects the slab kernel (the one these builds differ in)."""
+    lib = libs[0]
+    buf = ctypes.create_string_buffer(256)
+    binding.check(lib.mm_set_config(cfg.encode() if cfg else None), "mm_set_config")
+    try:
+        binding.check(lib.mm_describe_config(1 if form == "ffn" else 0, M, N, K, binding.LAYOUTS[layout],
+                                             buf, 256), "mm_describe_config")
+    finally:
+        binding.check(lib.mm_set_config(None), "mm_set_config")
+    assert "KERNEL=gemm_nt_slab" in buf.value.decode(), buf.value.decode()
+
+
+def run_both(libs, cfg, call, outs):
+    """Runs `call(lib)` with each build under the same configuration and
+    returns the outputs' bytes per build."""
+    got = []
+    for lib in libs:
+        binding.check(lib.mm_set_config(cfg.encode() if cfg else None), "mm_set_config")
+        try:
+            for o in outs:
+                o.view(torch.uint8).fill_(0xFF)
+            call(lib)
+            torch.cuda.synchronize()
+            got.append([o.view(torch.uint8).cpu().numpy().copy() for o in outs])
+        finally:
+            binding.check(lib.mm_set_config(None), "mm_set_config")
+    return got
+
+
+def assert_same(got):
+    (a, b) = got
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y), "the full-sync build differs from the normal build"
+
+
+def operands(M, N, K, layout, seed, dev):
+    a = synth.randn_bf16((M, K), 1.0, seed)
+    b = synth.randn_bf16((K, N), K ** -0.5, seed + 1)
+    A = a.t().contiguous() if layout[0] == "t" else a
+    B = b.t().contiguous() if layout[1] == "t" else b
+    return A.to(dev), B.to(dev)
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("grid", [0, 5])
+def test_linear_and_matmul_all_storages(libs, layout, grid):
+    dev = torch.device("cuda:0")
+    M, N, K = 1040, 776, 1024  # 5 x 4 tiles (ragged), 16 super-steps
+    cfg = SLAB + f",GRID={grid}"
+    A, B = operands(M, N, K, layout, 900 + grid, dev)
+    bias = synth.randn_bf16((N,), 1.0, 950).to(dev)
+    lay = binding.LAYOUTS[layout]
+    assert_slab(libs, cfg, "linear", M, N, K, layout)
+    say("linear bias+GELU", layout, (M, N, K), cfg)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
+        A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K, lay,
+        binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))
+    say("matmul f32", layout, (M, N, K), cfg)
+    out32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_matmul(
+        A.data_ptr(), B.data_ptr(), out32.data_ptr(), M, N, K, lay, 1, stream()), "mm_matmul"),
+        [out32]))
+
+
+@pytest.mark.parametrize("grid", [0, 7])
+def test_ffn_and_preact(libs, grid):
+    dev = torch.device("cuda:0")
+    M, N, K = 776, 1160, 768
+    x = synth.randn_bf16((M, K), 1.0, 960).to(dev)
+    Wg = synth.randn_bf16((N, K), K ** -0.5, 961).to(dev)
+    Wu = synth.randn_bf16((N, K), K ** -0.5, 962).to(dev)
+    bias = synth.randn_bf16((N,), 1.0, 963).to(dev)
+    cfg = f"BM=256,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
+    assert_slab(libs, cfg, "ffn", M, N, K, "nt")
+    assert_slab(libs, cfg, "linear", M, N, K, "nt")
+    say("ffn swiglu", (M, N, K), cfg)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_ffn_swiglu(
+        x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), out.data_ptr(), M, N, K, stream()),
+        "mm_ffn_swiglu"), [out]))
+    say("linear with pre-activation", (M, N, K), cfg)
+    pre = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear_preact(
+        x.data_ptr(), Wg.data_ptr(), bias.data_ptr(), out.data_ptr(), pre.data_ptr(), M, N, K,
+        binding.LAYOUTS["nt"], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear_preact"),
+        [out, pre]))
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("case", [(520, 392, 8192, None),
+                                  (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
+def test_splitk(libs, layout, case):
+    dev = torch.device("cuda:0")
+    M, N, K, cfg = case
+    A, B = operands(M, N, K, layout, 970, dev)
+    lay = binding.LAYOUTS[layout]
+    sizes = []
+    for lib in libs:
+        binding.check(lib.mm_set_config(cfg.encode() if cfg else None), "mm_set_config")
+        n = ctypes.c_int64(0)
+        binding.check(lib.mm_workspace_size(0, M, N, K, lay, ctypes.byref(n)), "mm_workspace_size")
+        binding.check(lib.mm_set_config(None), "mm_set_config")
+        sizes.append(n.value)
+    assert sizes[0] == sizes[1] > 0, "this shape should take the split-K path"
+    ws = torch.empty(sizes[0], dtype=torch.uint8, device=dev)
+    say("split-K", layout, (M, N, K), cfg, sizes[0])
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_matmul_ws(
+        A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lay, 1, ws.data_ptr(), ws.numel(),
+        stream()), "mm_matmul_ws"), [out]))
