@@ -110,7 +110,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
+        print(f"bench.py: measures one GPU only (asked for {max(args.gpus, world)}); "
               "the GEMM path has no multi-GPU mode", file=sys.stderr)
         return 2
 
