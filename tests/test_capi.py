@@ -5,7 +5,6 @@ and its tile order covers every output tile exactly once.
 No test here launches a kernel, and no call here passes validation with a
 pointer that is not real device memory.
 """
-import ctypes
 import os
 import re
 

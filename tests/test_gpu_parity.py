@@ -12,7 +12,6 @@
   that is not 16-byte aligned, guard bands around the output, repeatability,
   and an operand with more than 2^31 elements.
 """
-import ctypes
 
 import numpy as np
 import pytest
