@@ -151,7 +151,8 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * there and left out of the persistent scheduler).  When a plain product --
  * mm_matmul, or mm_linear with MM_EPI_NONE, any layout -- with K a
  * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
- * workgroups, the _ws entry points below cut each tile's K loop into chunks
+ * workgroups (at most half as many) and K long enough that each chunk spans
+ * at least 8 x 64 of it, the _ws entry points below cut each tile's K loop into chunks
  * and deal the chunks of all tiles to the resident workgroups (one chunk
  * each, or equal contiguous ranges: stream-K); each piece leaves its fp32
  * partial tile in this workspace (one 256 KiB slot per workgroup, two per
