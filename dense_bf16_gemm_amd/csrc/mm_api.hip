@@ -573,7 +573,10 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
              : k->pipe == 2 ? (int)cdiv(r.K, mmk::kPipeBK)
              : k->pipe == 1 ? (int)(2 * cdiv(r.K, 2 * mmk::kPipeBK))
                             : (int)cdiv(r.K, mmk::kBK);
-  p.group_m = c.group;
+  // A band taller than the tile rows is one band of all of them: clamped,
+  // the order is the same and tile_coords' band = group_m * tiles_n stays
+  // below the tile count (< 2^31) instead of wrapping for a forced G.
+  p.group_m = (int)(c.group < tm ? c.group : tm);
   p.xcd_remap = c.xcd;
   p.k_alt = k_alt_enabled(c, r.K) ? 1 : 0;
   p.sk_chunks = 1;

@@ -221,3 +221,20 @@ def test_preact_argument_checks():
         assert st == want, (p, epi, st)
     # an empty product is a successful no-op
     assert lib.mm_linear_preact(x, W, bias, out, pre, 0, N, K, nt, E["bias_gelu_tanh"], None) == 0
+
+
+def test_forced_band_height_is_clamped():
+    """A forced band height far above the tile rows (G = 2^20 with 4096 tile
+    columns: G * tiles_n would pass 2^32) gives the same order as one band of
+    all tile rows, and still visits every tile once."""
+    M, N, K = 128, 4096 * 64, 64
+    try:
+        binding.set_config("BM=64,BN=64,WM=2,WN=2,G=1048576,XCD=1,KALT=0")
+        big = binding.debug_schedule("matmul", M, N, K, 256)
+        binding.set_config("BM=64,BN=64,WM=2,WN=2,G=2,XCD=1,KALT=0")
+        two = binding.debug_schedule("matmul", M, N, K, 256)
+    finally:
+        binding.set_config(None)
+    assert big == two
+    assert len(big) == 2 * 4096
+    assert {(tm, tn) for (_, _, tm, tn, _) in big} == {(i, j) for i in range(2) for j in range(4096)}

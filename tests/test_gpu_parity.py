@@ -3,11 +3,12 @@
 * Index mapping, bit for bit: integer operands whose fp32 sums are exact in
   any order, every layout, every tile configuration, shapes that span
   several tiles with ragged M, N and K tails.
-* Numerics at the five workloads' real sizes and launch configuration
-  (the heuristic, exactly as the benchmark runs them): full outputs where the
-  oracle is quick, sampled outputs (random points plus every tile-boundary
-  row and column) elsewhere; bf16 outputs within 2e-2*(|ref|+1), fp32 outputs
-  within 1e-3*(|ref|+1).
+* Numerics at every workload's real size and launch configuration (the
+  heuristic and automatic split-K, exactly as the benchmark runs them):
+  every output element against the oracle's full output; bf16 outputs within
+  2e-2*(|ref|+1), fp32 outputs within 1e-3*(|ref|+1).
+* Index mapping at the same real shapes, storages and launches, bit for bit
+  over the whole output, with integer operands.
 * Edge cases: empty outputs, 1x1, unaligned fp32 rows, an output pointer
   that is not 16-byte aligned, guard bands around the output, repeatability,
   and an operand with more than 2^31 elements.
@@ -572,15 +573,35 @@ def test_ffn_swiglu_random(dev, cfg, K):
     assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
 
 
-def run_workload(w: synth.Workload, t, dev):
+GUARD_BYTES = 4096
+
+
+def guarded_out(M, N, f32, dev):
+    """An [M, N] output inside a buffer with 4 KiB guard bands of NaN bytes
+    on both sides (the output itself starts 4 KiB in: 16-byte aligned)."""
+    esize = 4 if f32 else 2
+    g = GUARD_BYTES // esize
+    buf = torch.full((M * N + 2 * g,), float("nan"), dtype=torch.float32 if f32 else torch.bfloat16,
+                     device=dev)
+    return buf, buf[g:g + M * N].view(M, N)
+
+
+def guards_intact(buf, M, N):
+    g = GUARD_BYTES // buf.element_size()
+    return bool(torch.isnan(buf[:g]).all()) and bool(torch.isnan(buf[g + M * N:]).all())
+
+
+def run_workload(w: synth.Workload, t, dev, out=None):
+    """One call of the workload exactly as bench.py makes it (the heuristic's
+    configuration, split-K through the automatic workspace where it applies)."""
     g = {k: v.to(dev) for k, v in t.items()}
     if w.form == "matmul":
         A = g["A"] if "A" in g else g["At"].t()  # transposed views, read in place
         B = g["B"] if "B" in g else g["Bt"].t()
-        return mm.matmul(A, B, torch.float32 if w.out_dtype == "f32" else torch.bfloat16)
+        return mm.matmul(A, B, torch.float32 if w.out_dtype == "f32" else torch.bfloat16, out=out)
     if w.form == "linear":
-        return mm.linear(g["x"], g["W"], g["bias"], w.epilogue)
-    return mm.ffn_swiglu(g["x"], g["W_gate"], g["W_up"])
+        return mm.linear(g["x"], g["W"], g["bias"], w.epilogue, out=out)
+    return mm.ffn_swiglu(g["x"], g["W_gate"], g["W_up"], out=out)
 
 
 def oracle_args(w: synth.Workload, t):
@@ -597,25 +618,86 @@ def oracle_args(w: synth.Workload, t):
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_parity(dev, name):
+    """Every output element of every workload at its real size, in the launch
+    configuration bench.py times, against the oracle's full output; the 4 KiB
+    around the output stay untouched."""
     w = synth.WORKLOADS[name]
     say("workload", name, binding.describe_config(w.form, w.M, w.N, w.K, w.layout))
     t = w.make()
-    out = run_workload(w, t, dev)
+    f32 = w.out_dtype == "f32"
+    buf, out = guarded_out(w.M, w.N, f32, dev)
+    run_workload(w, t, dev, out=out)
     torch.cuda.synchronize()
+    assert guards_intact(buf, w.M, w.N)
     got = out.float().cpu().numpy()
-    rel = 1e-3 if w.out_dtype == "f32" else 2e-2
-    args = oracle_args(w, t)
-    if w.M * w.N * w.K <= 2 ** 28:
-        y, _ = oracle.gemm(**args)
-        assert tol_excess(got, y, rel) <= 0
+    del buf, out
+    y, _ = oracle.gemm(**oracle_args(w, t))
+    assert tol_excess(got, y, 1e-3 if f32 else 2e-2) <= 0
+
+
+def mapping_case(w: synth.Workload):
+    """The integer-operand form of a workload at its real shape and storage:
+    sparse +-1 rows against integers in [-4, 4] (bias in [-64, 64]) for bf16
+    outputs, dense integers in [-2, 2] for fp32 outputs; linear workloads take
+    the bias epilogue and the FFN the identity gate (g * u), whose results
+    are exact small integers.  Returns (operands in storage layout, oracle
+    keyword arguments, the call on the GPU)."""
+    seed = (w.M * 31 + w.N * 7 + w.K) % 100003
+    if w.out_dtype == "f32":
+        A, B = synth.dense_int_operands(w.M, w.N, w.K, w.layout, seed)
+        ops = dict(A=A, B=B)
+        kw = dict(A=synth.bits(A), B=synth.bits(B), layout=w.layout, epilogue="none")
+    elif w.form == "ffn":
+        ops = synth.mapping_operands(w.M, w.N, w.K, "nt", seed, gated=True)
+        ops = dict(A=ops["A"], B=ops["B"], B2=ops["B2"])
+        kw = dict(A=synth.bits(ops["A"]), B=synth.bits(ops["B"]), B2=synth.bits(ops["B2"]),
+                  layout="nt", epilogue="glu_identity")
     else:
-        rows, cols = synth.sample_points(w.M, w.N, 3000, seed=w.M + w.N)
-        y, _ = oracle.points(rows=rows, cols=cols, **args)
-        assert tol_excess(got[rows, cols], y, rel) <= 0
-        # and whole rows at the first and last tile band
-        for r0 in (0, w.M - 3):
-            yr, _ = oracle.gemm(rows=(r0, r0 + 3), **args)
-            assert tol_excess(got[r0:r0 + 3], yr, rel) <= 0
+        bias = w.form == "linear"
+        o = synth.mapping_operands(w.M, w.N, w.K, w.layout, seed, with_bias=bias)
+        ops = dict(A=o["A"], B=o["B"])
+        kw = dict(A=synth.bits(o["A"]), B=synth.bits(o["B"]), layout=w.layout,
+                  epilogue="bias" if bias else "none")
+        if bias:
+            ops["bias"] = o["bias"]
+            kw["bias"] = synth.bits(o["bias"])
+    return ops, kw
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_mapping_bitexact(dev, name):
+    """Tile order, index mapping and K slicing bit for bit at each workload's
+    real shape, storage and launch configuration (persistent grid, XCD remap,
+    band order, K alternation, automatic split-K): integer operands whose
+    fp32 sums are exact in any order, every output element compared with the
+    oracle's bits, guard bands checked."""
+    w = synth.WORKLOADS[name]
+    say("workload mapping", name, binding.describe_config(w.form, w.M, w.N, w.K, w.layout))
+    ops, kw = mapping_case(w)
+    f32 = w.out_dtype == "f32"
+    buf, out = guarded_out(w.M, w.N, f32, dev)
+    g = {k: v.to(dev) for k, v in ops.items()}
+    lay = w.layout
+    if w.form == "ffn":
+        call_ffn(g["A"], g["B"], g["B2"], w.M, w.N, w.K, "identity", out)
+    else:
+        # the bench's call: torch views of the stored operands, read in place
+        A = g["A"].t() if lay[0] == "t" else g["A"]
+        B = g["B"].t() if lay[1] == "t" else g["B"]
+        if w.form == "linear":
+            mm.linear(A, g["B"], g["bias"], "bias", out=out)
+        else:
+            mm.matmul(A, B, torch.float32 if f32 else torch.bfloat16, out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, w.M, w.N)
+    got = out.cpu()
+    del buf, out, g
+    ref, ref_bits = oracle.gemm(**kw)
+    if f32:
+        bad = np.argwhere(got.numpy() != ref)
+    else:
+        bad = np.argwhere(to_bits(got) != ref_bits)
+    assert bad.size == 0, f"{name}: {len(bad)} mismatches, first {bad[:5].tolist()}"
 
 
 # ------------------------------------------------------------ edge cases
