@@ -6,13 +6,21 @@
 A step is one call of the fused operation on one batch of synthetic input
 already resident in device memory (default: linear + bias + GELU(tanh) at
 M = N = K = 8192, W stored [N][K]).  Prints ONE JSON line with the throughput
-in TFLOP/s (2*M*N*K flops per GEMM) once the clocks have settled (the
-first launches after idle run at boost clocks, then the board's power limit
-takes over within about 100 launches), a roofline object for the GEMM kernel
-(achieved TFLOP/s from HIP events around every launch on the launch stream,
-in a second pass of the same number of launches after the timed region,
-against the bf16 dense MFMA peak) and the CPU oracle's throughput on a
-bounded sample of the same workload, timed on this host's cores.
+in TFLOP/s (2*M*N*K flops per GEMM) over K timed steps, a roofline object for
+the GEMM kernel (achieved TFLOP/s from HIP events around every launch on the
+launch stream, in a second pass of the same number of launches after the
+timed region, against the bf16 dense MFMA peak) and the CPU oracle's
+throughput on a bounded sample of the same workload, timed on this host's
+cores.
+
+Settling.  After idle the GPU's clock ramps up over the first few tens of
+milliseconds of work: at 8192^3, launches 5-25 after two idle seconds took
+786 us on average (max 926), launches 25-45 715 us, and from about launch 45
+on 693-697 us, flat to launch 3000.  So the W warm-up launches are followed,
+when they are fewer, by more untimed launches until at least SETTLE_LAUNCHES
+launches and SETTLE_SECONDS of launches have run; the JSON line reports that
+settle phase ("settle": its extra launches, its length, and the mean launch
+time of its first and last windows) beside "warmup".
 """
 from __future__ import annotations
 
@@ -30,6 +38,10 @@ sys.path.insert(0, ROOT)
 # MI355X bf16 dense MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz (published as 2.5 PFLOP/s)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
+# floor of the untimed launches before the timed region (see Settling above)
+SETTLE_LAUNCHES = 100
+SETTLE_SECONDS = 0.5
+SETTLE_WINDOW = 20
 CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 
@@ -150,9 +162,38 @@ def main() -> int:
     else:
         step = lambda: mm.ffn_swiglu(t["x"], t["W_gate"], t["W_up"], out=out)  # noqa: E731
 
+    stream = torch.cuda.current_stream()  # the stream every launch goes to
+    settle_t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
-    stream = torch.cuda.current_stream()  # the stream every launch goes to
+    # settle: windows of launches, each between one event pair, until the
+    # floor is reached (none if the warm-up already reached it); one window
+    # stays queued behind the one the host waits for, so the GPU never idles
+    done, extra, windows, pending = args.warmup, 0, [], []
+    while done < SETTLE_LAUNCHES or time.perf_counter() - settle_t0 < SETTLE_SECONDS:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(SETTLE_WINDOW):
+            step()
+        e1.record(stream)
+        pending.append((e0, e1))
+        done += SETTLE_WINDOW
+        extra += SETTLE_WINDOW
+        if len(pending) > 1:
+            a, b = pending.pop(0)
+            b.synchronize()
+            windows.append(a.elapsed_time(b) * 1e3 / SETTLE_WINDOW)
+    for a, b in pending:
+        b.synchronize()
+        windows.append(a.elapsed_time(b) * 1e3 / SETTLE_WINDOW)
+    settle = {
+        "extra_launches": extra,
+        "seconds": round(time.perf_counter() - settle_t0, 3),
+        "rule": f">= {SETTLE_LAUNCHES} launches and >= {SETTLE_SECONDS} s of launches before timing",
+        "first_window_us": round(windows[0], 1) if windows else None,
+        "last_window_us": round(windows[-1], 1) if windows else None,
+    }
     # Timed region: the K steps back to back, with one event pair around all
     # of them (events between launches would add their own gaps to it).
     torch.cuda.synchronize()
@@ -211,6 +252,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
