@@ -25,7 +25,7 @@ EXPORTS = (
     "mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
     "mm_describe_config", "mm_debug_schedule", "mm_status_string", "mm_last_error",
     "mm_workspace_size", "mm_matmul_ws", "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched",
-    "mm_linear_preact",
+    "mm_linear_preact", "mm_matmul_noalloc",
 )
 
 _lib = None
@@ -61,6 +61,7 @@ def open_library(path: str):
     lib.mm_ffn_glu.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
     lib.mm_workspace_size.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(ctypes.c_int64)]
     lib.mm_matmul_ws.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp, i64, vp]
+    lib.mm_matmul_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.mm_linear_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp, i64, vp]
     lib.mm_matmul_batched.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
     lib.mm_linear_batched.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
@@ -71,7 +72,8 @@ def open_library(path: str):
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("mm_matmul", "mm_linear", "mm_ffn_swiglu", "mm_ffn_glu", "mm_set_config",
                  "mm_describe_config", "mm_debug_schedule", "mm_workspace_size", "mm_matmul_ws",
-                 "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched", "mm_linear_preact"):
+                 "mm_linear_ws", "mm_matmul_batched", "mm_linear_batched", "mm_linear_preact",
+                 "mm_matmul_noalloc"):
         getattr(lib, name).restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p

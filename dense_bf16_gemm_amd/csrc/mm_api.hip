@@ -25,6 +25,16 @@
 #include "gemm_ws.hpp"
 #include "gemm_nt_slab.hpp"
 
+// Split-K partial tiles of mm_matmul_noalloc: a fixed device array instead of
+// a caller's workspace, for callers that cannot allocate.  64 MiB = one
+// 256 x 256 fp32 slot for each of 256 workgroups (a chunk-major split on a
+// 256-CU GPU).  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: the host uses the address hipGetSymbolAddress returns
+// for the current device.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -297,6 +307,29 @@ mm_status device_cus(int* cus) {
   return MM_OK;
 }
 
+// Device address of the static scratch on the current device, taken once per
+// device with that device current (each GPU holds its own copy of the array
+// at its own address).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mm_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MM_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MM_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MM_OK;
+}
+
 mm_status kernel_occupancy(KernelEntry* k, int* occ) {
   int o = k->occupancy.load(std::memory_order_relaxed);
   if (o == 0) {
@@ -330,6 +363,7 @@ struct Request {
   int64_t batch = 1;      // batched form: entries and their element strides
   int64_t stride_a = 0, stride_b = 0, stride_out = 0;
   void* out_pre = nullptr;  // second output: the pre-activation (GELU epilogues)
+  bool static_ws = false;   // ws is the library's static scratch (mm_matmul_noalloc)
 };
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -610,6 +644,11 @@ mm_status run(const Request& r, void* stream) {
     if ((s = kernel_occupancy(sk, &sk_occ)) != MM_OK) return s;
     sp = splitk_plan(r, c, splitk_wgs(c, cus, sk_occ));
     if (sp.n > 1) {
+      if (r.static_ws && r.ws_bytes < splitk_ws_bytes(sp))
+        return fail(MM_ERR_UNSUPPORTED,
+                    "this shape's split-K needs " + std::to_string(splitk_ws_bytes(sp)) +
+                        " bytes of scratch, more than the static scratch's " +
+                        std::to_string(r.ws_bytes) + " (use mm_matmul_ws with a workspace)");
       if (r.ws_bytes < splitk_ws_bytes(sp))
         return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
       if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
@@ -764,6 +803,22 @@ mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64
     return fail(MM_ERR_INVALID_VALUE, "bad output dtype");
   Request r{A, B, nullptr, nullptr, out, M, N, K, (int)layout, mmk::EPI_NONE,
             out_dtype == MM_OUT_F32, false, workspace, workspace ? workspace_bytes : 0};
+  return run(r, stream);
+}
+
+mm_status mm_matmul_noalloc(const void* A, const void* B, void* out, int64_t M, int64_t N,
+                            int64_t K, mm_layout layout, mm_out_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  if (out_dtype != MM_OUT_BF16 && out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_INVALID_VALUE, "bad output dtype");
+  Request r{A, B, nullptr, nullptr, out, M, N, K, (int)layout, mmk::EPI_NONE,
+            out_dtype == MM_OUT_F32, false};
+  // argument errors first, before any HIP call
+  mm_status s = validate(r);
+  if (s != MM_OK || M == 0 || N == 0) return s;
+  if ((s = scratch_address(&r.ws)) != MM_OK) return s;
+  r.ws_bytes = kScratchBytes;
+  r.static_ws = true;
   return run(r, stream);
 }
 

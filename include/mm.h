@@ -36,7 +36,8 @@
  *     more than 2^31 elements (addresses are formed in 64 bits).
  *   - Thread safety: calls may be made from several host threads; the only
  *     process-wide state is a per-device attribute cache, the configuration
- *     override (mm_set_config) and the thread-local last-error string.
+ *     override (mm_set_config), the thread-local last-error string and the
+ *     static split-K scratch of mm_matmul_noalloc (see there).
  */
 #ifndef MM_H_
 #define MM_H_
@@ -180,6 +181,25 @@ mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64
 mm_status mm_linear_ws(const void* x, const void* W, const void* bias, void* out, int64_t M,
                        int64_t N, int64_t K, mm_layout layout, mm_epilogue epi, void* workspace,
                        int64_t workspace_bytes, void* stream);
+
+/* mm_matmul_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the split-K partial tiles go to a static device array inside the library
+ * instead of a caller's workspace.  The array holds 64 MiB (one 256 x 256
+ * fp32 slot per workgroup of a chunk-major split on 256 CUs; the automatic
+ * split never needs more there); each GPU the library runs on holds its own
+ * copy from the first call on it until the process ends.  Arguments, results
+ * and errors as for mm_matmul; in addition a shape whose split needs more
+ * scratch than the array holds (a forced stream-K configuration) returns
+ * MM_ERR_UNSUPPORTED before any launch.  The call itself allocates nothing:
+ * no hipMalloc / hipFree, no allocating library routine.
+ * All calls on one GPU share its array, and a call reads only slots it has
+ * written itself, so calls made one after the other (on one stream, or
+ * synchronized) need no clearing between them; calls whose kernels may run
+ * at the same time on one GPU (two streams, two host threads) race on the
+ * array and must not be made.                                               */
+mm_status mm_matmul_noalloc(const void* A, const void* B, void* out, int64_t M, int64_t N,
+                            int64_t K, mm_layout layout, mm_out_dtype out_dtype, void* stream);
 
 /* Llama-FFN horizontal fusion in one kernel:
  *   out[M][N] = SiLU(x . W_gate^T) * (x . W_up^T), bf16 output (RNE),
