@@ -231,15 +231,19 @@ def main() -> int:
     # into split-K: the slab kernel's split-K instance, then splitk_reduce
     splitk = (w.form != "ffn" and w.epilogue == "none"
               and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
+    bkn = str(w.layout in ("nn", "tn")).lower()
+    amk = str(w.layout in ("tn", "tt")).lower()
     if splitk:
-        kernel = "mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, false, false> + mmk::splitk_reduce"
+        # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights,
+        # [K][M] activations, bias staged in LDS>
+        kernel = (f"mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, {bkn}, {amk}, false> + "
+                  "mmk::splitk_reduce")
         tiles = "BM=256,BN=256,WM=2,WN=2,SPLITK,KERNEL=gemm_nt_slab+splitk_reduce"
     elif cfg["KERNEL"] == "gemm_nt_slab":
-        # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights, [K][M] activations>
-        bkn = str(w.layout in ("nn", "tn")).lower()
-        amk = str(w.layout in ("tn", "tt")).lower()
+        bstage = str(cfg.get("BSTAGE") == "1" and w.form == "linear" and "bias" in w.epilogue
+                     and w.layout == "nt").lower()
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
-                  f"false, false, {bkn}, {amk}>")
+                  f"false, false, {bkn}, {amk}, {bstage}>")
     elif cfg["KERNEL"] == "gemm_ws":
         kernel = "mmk::gemm_ws"
     else:

@@ -151,7 +151,7 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false,
-          bool BKN = false, bool AMK = false>
+          bool BKN = false, bool AMK = false, bool BSTAGE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
   // BKN: the weight operand is stored [K][N] (the MatmulOp form's B as
@@ -163,6 +163,9 @@ gemm_nt_slab(GemmParams p) {
   // AMK: the activation operand is stored [K][M] (M contiguous), handled the
   // same way: 64 k-rows of 256 rows' values per slab, transpose reads.
   static_assert(!(AMK && (FFN || PRE)), "[K][M] activations in the single-weight form only");
+  // BSTAGE: the instance whose K loop also brings each tile's bias into LDS
+  // (see copy_bias); built for the K-contiguous linear form with bias.
+  static_assert(!(BSTAGE && (FFN || SPLITK || PRE || BKN || AMK)), "bias staging: plain linear form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
@@ -458,6 +461,9 @@ gemm_nt_slab(GemmParams p) {
     }
   };
 
+  const bool has_bias = (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU);
+  const bool bias_vec = (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
+
   // ---- ring: super-step q (counted over all tiles of this workgroup) has
   // its A slab in unit (2q) % 5 and its weight slab in unit (2q + 1) % 5.
   int cur_unit = 0;  // A unit of the current super-step
@@ -490,6 +496,38 @@ gemm_nt_slab(GemmParams p) {
   // fragment read last in a k-step is needed four rows into the next one
   // and no k-step starts by waiting on LDS.
   uint32_t a_cur = a_x0, b_cur = b_x0 + (uint32_t)UNIT;  // units of super-step q
+  // BSTAGE: epilogue inputs prefetched under the K loop (issue "Automate
+  // performant Hopper matmul", section "Epilogue inputs").  The registers have
+  // no room for them during the K loop (holding a tile's bias vectors across
+  // it spilled 221 registers), but LDS has, at one moment of every
+  // super-step: after its mid-step barrier no wave reads q's weight unit again
+  // until the next super-step copies into it.  So in the k-step after that
+  // barrier, among its weight copies, each wave copies its 128 columns of the
+  // tile's bias (256 bytes) straight from global memory into two of its own
+  // 1 KiB blocks of that unit.  The next super-step's first two activation
+  // copies of the same wave overwrite those blocks (a wave's later copies land
+  // later); the copy of a tile's last super-step survives into the epilogue,
+  // which reads the bias back from LDS after a wait that leaves the weight
+  // copies issued after it (the next tile's) in flight.  Every super-step
+  // does it, with a record of 0 bytes (nothing fetched) when the tile's bias
+  // is not staged, so the loop has no branch for it (a branch, or a peeled
+  // last super-step, changed the loop's register allocation).  A copy is one
+  // 16-byte load per lane at the copies' lane offsets: lanes 0..7 (row 0)
+  // fetch the 8 chunks of a 128-byte half, permuted by the row swizzle; the
+  // other lanes' offsets lie past the 128-byte record and fill the rest of
+  // the block with zeros.
+  int bias_n0 = -1;  // first column of this tile if its bias goes through LDS, else -1
+  auto copy_bias = [&](int unit) __attribute__((always_inline)) {
+    const uint64_t bb = reinterpret_cast<uint64_t>(p.bias) + 2u * (uint32_t)(bias_n0 + wrow_b);
+    const uint32_t rec = bias_n0 >= 0 ? 128u : 0u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(bb + 128u * h, rec);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (h * NW + wave) * 1024), 16,
+          lane_base, 0, 0, 0);
+    }
+  };
   auto super_step = [&](int k0_fetch) __attribute__((always_inline)) {
     const uint32_t kbytes = 2u * (uint32_t)k0_fetch;
     const int ua = cur_unit, ub = next_unit(ua);
@@ -551,6 +589,8 @@ gemm_nt_slab(GemmParams p) {
       mfma_half(r, 1, 0);
       if (p == 1) copy_b(0, kbytes, cub);
       copy_b(p, kbytes, cub);
+      if constexpr (BSTAGE)
+        if (p == 2) copy_bias(ub);  // five weight copies follow it
       if (p <= FN / 2) {
         read_b(0, 2 * (p - 1), 0, b_nxt);
         read_b(0, 2 * (p - 1) + 1, 0, b_nxt);
@@ -583,9 +623,7 @@ gemm_nt_slab(GemmParams p) {
   // 128-byte output line are stored back to back.  F32 / ACT / CHECKED are
   // compile-time in the fast paths (interior tiles with aligned rows) and
   // run-time in the one checked path for edge tiles.
-  const bool has_bias = (p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU);
   const bool act_on = FFN ? (p.epi == EPI_SWIGLU) : (p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU);
-  const bool bias_vec = (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
   constexpr int PAIRS = FFN ? FN / 4 : FN / 2;
   void* obase = p.out;  // output of the current batch entry
   // 8 consecutive outputs of row m from column n on: one 16-byte (bf16) or
@@ -631,7 +669,29 @@ gemm_nt_slab(GemmParams p) {
     // same for the whole wave) loads all of its bias vectors before the first
     // wait; other tiles check each lane's columns.
     const bool bias_fast = !FFN && has_bias && bias_vec && n0 + OUT_BN <= N;
-    if (bias_fast) {
+    if (BSTAGE && bias_n0 >= 0) {
+      // the bias staged in LDS by the last super-step (copy_bias): logical
+      // 16-byte chunk 4 pr + lk of the wave's 256 bytes sits in block pr / 2,
+      // at physical chunk ((4 pr + lk) & 7) ^ s, s the row-0 swizzle of the
+      // copies; five weight copies were issued after it
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS - 3));
+      const int bunit = cur_unit == 0 ? kSlabUnits - 1 : cur_unit - 1;
+      const int bsw = lds_swz(8 * (wave & 2));
+      u32x4 w[PAIRS];
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        ncol[pr] = n0 + wrow_b + 32 * pr + 8 * lk;
+        w[pr] = *reinterpret_cast<const u32x4*>(smem + bunit * UNIT + ((pr >> 1) * NW + wave) * 1024 +
+                                                 16 * (((4 * pr + lk) & 7) ^ bsw));
+      }
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bv[pr][2 * j] = __builtin_bit_cast(float, w[pr][j] << 16);
+          bv[pr][2 * j + 1] = __builtin_bit_cast(float, w[pr][j] & 0xffff0000u);
+        }
+    } else if (bias_fast) {
       u32x4 w[PAIRS];
 #pragma unroll
       for (int pr = 0; pr < PAIRS; ++pr) {
@@ -737,6 +797,14 @@ gemm_nt_slab(GemmParams p) {
     const TileDesc nxt = tile_desc(tile_i + 1 < my_tiles ? tile_i + 1 : tile_i);
     int h_tile, h_slice, h_kbeg, nks;
     unit_of(tile_i, &h_tile, &h_slice, &h_kbeg, &nks);
+    int tm, tn;
+    if constexpr (BSTAGE) {
+      // a tile whose columns all lie inside N, with a 16-byte aligned bias
+      // (the same for the whole wave), stages its bias through LDS; other
+      // tiles load it in the epilogue
+      tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+      bias_n0 = (has_bias && bias_vec && (tn + 1) * OUT_BN <= N) ? tn * OUT_BN : -1;
+    }
     __builtin_amdgcn_s_waitcnt(kLgkmDrained);
     for (int ks = 0; ks < nks; ++ks) {
       int lks = ks + 2;
@@ -755,8 +823,7 @@ gemm_nt_slab(GemmParams p) {
       continue;
     }
 
-    int tm, tn;
-    tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    if constexpr (!BSTAGE) tile_coords(h_tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * OUT_BN;
     obase = static_cast<char*>(p.out) + (int64_t)h_slice * p.stride_out * (p.out_f32 ? 4 : 2);
     using T = std::true_type;

@@ -57,6 +57,7 @@ struct KernelEntry {
   std::atomic<int> occupancy;  // resident workgroups per CU, 0 = not queried
   bool splitk = false;         // gemm_nt_slab<..., SPLITK>: needs a workspace
   bool pre = false;            // gemm_nt_slab<..., PRE>: stores the pre-activation too
+  bool bstage = false;         // gemm_nt_slab<..., BSTAGE>: stages the bias through LDS
 };
 
 #define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
@@ -92,6 +93,13 @@ struct KernelEntry {
   {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC)>), {0}}
 
+// the plain linear form with the bias brought into LDS under the K loop
+#define MM_KSB()                                                                           \
+  {256, 256, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, false, false, true>),       \
+   {0}, false, false, true}
+
 #define MM_KWS()                                                                           \
   {256, 128, 2, 4, true, true, false, 4, reinterpret_cast<const void*>(&mmk::gemm_ws), {0}}
 
@@ -108,6 +116,7 @@ KernelEntry g_kernels[] = {
     MM_KSK(false, false),
     MM_KSK(false, true),
     MM_KSP(),
+    MM_KSB(),
     MM_KWS(),
     MM_KS(false),
     MM_KS(true),
@@ -131,10 +140,11 @@ KernelEntry g_kernels[] = {
 };
 
 KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe,
-                         bool splitk = false, bool pre = false) {
+                         bool splitk = false, bool pre = false, bool bstage = false) {
   for (auto& k : g_kernels)
     if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
-        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk && k.pre == pre)
+        k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk && k.pre == pre &&
+        k.bstage == bstage)
       return &k;
   return nullptr;
 }
@@ -151,6 +161,7 @@ struct Config {
   int pipe = 3;   // preferred kernel family: 4 wave-specialized (BN=128, WN=4), 3 slab ring,
                   // 2 ping-pong, 1 pipeline, 0 basic
   int sk = 0;     // split-K slices when a workspace is given: 0 automatic, 1 off, n forced
+  int bstage = 0; // 1: linear forms with a bias take the slab instance that stages it in LDS
   bool forced = false;  // set by mm_set_config / MM_FORCE_CONFIG (not by the heuristic)
 };
 
@@ -185,9 +196,10 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "GRID") c.grid = (int)v;
     else if (key == "PIPE") c.pipe = (int)v;
     else if (key == "SK") c.sk = (int)v;
+    else if (key == "BSTAGE") c.bstage = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 4 || c.sk > 64) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 4 || c.sk > 64 || c.bstage > 1) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -569,7 +581,11 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // 64 k-rows of such an operand with 32-bit buffer offsets
     if (fam == 3 && !b_kc && (int64_t)mmk::kSlabK * r.N * 2 >= (int64_t(1) << 31)) continue;
     if (fam == 3 && !a_kc && (int64_t)mmk::kSlabK * r.M * 2 >= (int64_t(1) << 31)) continue;
-    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre);
+    // the bias-staging instance: K-contiguous single-weight linear forms
+    // with a bias epilogue, when the configuration asks for it
+    const bool bstage = fam == 3 && c.bstage && a_kc && b_kc && !r.ffn && !r.out_pre && r.batch == 1 &&
+                        (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
+    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre, bstage);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile
   if (!k) k = find_kernel(c.bm, c.bn, 2, 2, a_kc, b_kc, r.ffn, 0);
@@ -886,8 +902,9 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
     g_last_error.clear();
   }
   std::snprintf(buf, (size_t)buflen,
-                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,KERNEL=%s", c.bm, c.bn,
-                c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe, kernel);
+                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,%sKERNEL=%s", c.bm, c.bn,
+                c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe,
+                c.bstage ? "BSTAGE=1," : "", kernel);
   return MM_OK;
 }
 

@@ -37,6 +37,10 @@ CONFIGS = [
     "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=4",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
+    # the slab instance that brings each tile's bias into LDS under the K
+    # loop (bias epilogues of K-contiguous shapes with whole super-steps),
+    # on a small grid so that the staging runs across several tiles
+    "BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3,BSTAGE=1",
 ]
 FFN_CONFIGS = [
     "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,PIPE=3",
@@ -848,3 +852,24 @@ def test_int64_transposed_storage(dev, layout):
         y, _ = oracle.gemm(synth.bits(Ah), synth.bits(tail), "nn")
         got = out[:, N - 64:].cpu().numpy()
     assert tol_excess(got, y, 1e-3) <= 0
+
+
+def test_bias_staged_workload_mapping(dev):
+    """The bias-staging instance at the 8192^3 linear workload's real shape and
+    launch (BSTAGE=1 on the heuristic's tile order): integer operands, bias
+    epilogue, every output bit equal to the oracle's."""
+    w = synth.WORKLOADS["linear_bias_gelu_8192"]
+    cfg = binding.describe_config(w.form, w.M, w.N, w.K, w.layout).rsplit(",KERNEL=", 1)[0] + ",BSTAGE=1"
+    binding.set_config(cfg)
+    say("bias staged mapping", cfg)
+    ops, kw = mapping_case(w)
+    buf, out = guarded_out(w.M, w.N, False, dev)
+    g = {k: v.to(dev) for k, v in ops.items()}
+    mm.linear(g["A"], g["B"], g["bias"], "bias", out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, w.M, w.N)
+    got = out.cpu()
+    del buf, out, g
+    _, ref_bits = oracle.gemm(**kw)
+    bad = np.argwhere(to_bits(got) != ref_bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"

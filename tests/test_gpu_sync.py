@@ -151,3 +151,22 @@ def test_splitk(libs, layout, case):
     assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_matmul_ws(
         A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, lay, 1, ws.data_ptr(), ws.numel(),
         stream()), "mm_matmul_ws"), [out]))
+
+
+@pytest.mark.parametrize("grid", [0, 5])
+def test_linear_bias_staged(libs, grid):
+    """The instance that brings each tile's bias into LDS under the K loop
+    (BSTAGE=1): ragged tiles load their bias in the epilogue, interior tiles
+    read it from LDS."""
+    dev = torch.device("cuda:0")
+    M, N, K = 1040, 776, 1024
+    cfg = SLAB + f",GRID={grid},BSTAGE=1"
+    A, B = operands(M, N, K, "nt", 980 + grid, dev)
+    bias = synth.randn_bf16((N,), 1.0, 985).to(dev)
+    assert_slab(libs, cfg, "linear", M, N, K, "nt")
+    for epi in ("bias", "bias_gelu_tanh"):
+        say("linear, bias staged", epi, (M, N, K), cfg)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
+            A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
+            binding.LAYOUTS["nt"], binding.EPILOGUES[epi], stream()), "mm_linear"), [out]))

@@ -29,6 +29,13 @@ REG_FILE = 512  # VGPRs + AGPRs per lane at one wave per SIMD
 # above the present counts (at most 7 VGPR and 6 SGPR dwords): a change that
 # spills more fails here and is looked at.
 SPILL_BUDGET_256ACC = {"VGPRs Spill": 8, "SGPRs Spill": 8, "ScratchSize [bytes/lane]": 32}
+# The bias-staging slab instance (selected only by configuration) keeps the
+# staging state in scalar registers across its K loop; its scalar spills go
+# to vector-register lanes outside the loop (test_no_lane_spills_in_mfma_loops).
+SPILL_BUDGET_OVERRIDE = {
+    "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb1EEEvNS_10GemmParamsE":
+        {"SGPRs Spill": 12},
+}
 
 
 def _tool(name: str) -> str:
@@ -272,6 +279,7 @@ def test_spills_within_budget(remarks):
     for name, r in remarks.items():
         if r["AGPRs"] >= 256:
             for key, cap in SPILL_BUDGET_256ACC.items():
+                cap = SPILL_BUDGET_OVERRIDE.get(name, {}).get(key, cap)
                 assert r[key] <= cap, (name, key, r[key])
         else:
             for key in SPILL_BUDGET_256ACC:
@@ -291,10 +299,20 @@ def test_no_scratch_in_mfma_loops(disassembly):
     assert checked >= 10
 
 
+def test_no_lane_spills_in_mfma_loops(disassembly):
+    """Scalar-register spills (to and from vector-register lanes) stay out of
+    every K loop as well."""
+    for name, code in disassembly.items():
+        if not any(_is_mfma(m) for (_, m, _) in code):
+            continue
+        for body in _k_loops(code):
+            assert not any(m in ("v_writelane_b32", "v_readlane_b32") for m in body), name
+
+
 def test_headline_kernel_k_loop_shape(disassembly):
     """The 256 x 256 slab kernel's K loop: 128 MFMAs per 64-k super-step (a
     multiple of it if unrolled), one barrier per super-step, no scratch."""
-    name = "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0EEEvNS_10GemmParamsE"
+    name = "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb0EEEvNS_10GemmParamsE"
     code = disassembly[name]
     loops = _k_loops(code)
     assert len(loops) == 1, len(loops)
