@@ -244,8 +244,8 @@ def main() -> int:
                      and w.layout == "nt").lower()
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
                   f"false, false, {bkn}, {amk}, {bstage}>")
-    elif cfg["KERNEL"] == "gemm_ws":
-        kernel = "mmk::gemm_ws"
+    elif cfg["KERNEL"] in ("gemm_ws", "gemm_pp"):
+        kernel = f"mmk::{cfg['KERNEL']}"
     else:
         kernel = f"mmk::{cfg['KERNEL']}<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}>"
     result = {

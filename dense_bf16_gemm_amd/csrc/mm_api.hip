@@ -23,6 +23,7 @@
 #include "gemm_nt_pipe.hpp"
 #include "gemm_pingpong.hpp"
 #include "gemm_ws.hpp"
+#include "gemm_pp.hpp"
 #include "gemm_nt_slab.hpp"
 
 // Split-K partial tiles of mm_matmul_noalloc: a fixed device array instead of
@@ -50,7 +51,8 @@ mm_status fail(mm_status s, const std::string& msg) {
 struct KernelEntry {
   int bm, bn, wgm, wgn;
   bool a_kc, b_kc, ffn;
-  int pipe;  // 4: wave-specialized (gemm_ws), 3: whole-line slab ring (gemm_nt_slab),
+  int pipe;  // 5: two-group ping-pong (gemm_pp), 4: wave-specialized (gemm_ws),
+             // 3: whole-line slab ring (gemm_nt_slab),
              // 2: ping-pong (gemm_pingpong),
              // 1: K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
   const void* fn;
@@ -103,6 +105,9 @@ struct KernelEntry {
 #define MM_KWS()                                                                           \
   {256, 128, 2, 4, true, true, false, 4, reinterpret_cast<const void*>(&mmk::gemm_ws), {0}}
 
+#define MM_KPPT()                                                                          \
+  {256, 128, 2, 4, true, true, false, 5, reinterpret_cast<const void*>(&mmk::gemm_pp), {0}}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
@@ -118,6 +123,7 @@ KernelEntry g_kernels[] = {
     MM_KSP(),
     MM_KSB(),
     MM_KWS(),
+    MM_KPPT(),
     MM_KS(false),
     MM_KS(true),
     MM_KPP(false),
@@ -158,8 +164,8 @@ struct Config {
   int xcd = 1;    // XCD-aware remap
   int kalt = 2;   // 0 never, 1 always, 2 automatic
   int grid = 0;   // 0 = CUs x occupancy
-  int pipe = 3;   // preferred kernel family: 4 wave-specialized (BN=128, WN=4), 3 slab ring,
-                  // 2 ping-pong, 1 pipeline, 0 basic
+  int pipe = 3;   // preferred kernel family: 5 two-group ping-pong, 4 wave-specialized (both
+                  // BN=128, WN=4), 3 slab ring, 2 split-phase, 1 pipeline, 0 basic
   int sk = 0;     // split-K slices when a workspace is given: 0 automatic, 1 off, n forced
   int bstage = 0; // 1: linear forms with a bias take the slab instance that stages it in LDS
   bool forced = false;  // set by mm_set_config / MM_FORCE_CONFIG (not by the heuristic)
@@ -199,7 +205,7 @@ bool parse_config(const char* spec, Config* out) {
     else if (key == "BSTAGE") c.bstage = (int)v;
     else return false;
   }
-  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 4 || c.sk > 64 || c.bstage > 1) return false;
+  if (c.group < 1 || c.xcd > 1 || c.kalt > 2 || c.pipe > 5 || c.sk > 64 || c.bstage > 1) return false;
   // the tile shape must be one that is instantiated (for some layout/form)
   bool any = false;
   for (auto& k : g_kernels)
@@ -561,9 +567,10 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   // the wave-specialized kernel (a configuration override for comparison)
   // takes single-weight K-contiguous products with whole super-steps; other
   // shapes run the default tile under that override
-  if (c.pipe == 4 && !(b_kc && a_kc && !r.ffn && r.batch == 1 && !r.out_pre && !sk &&
-                       r.K % mmk::kSlabK == 0 && r.K >= 2 * mmk::kSlabK &&
-                       (int64_t)256 * r.K * 2 < (int64_t(1) << 31))) {
+  // as does the two-group ping-pong kernel
+  if ((c.pipe == 4 || c.pipe == 5) &&
+      !(b_kc && a_kc && !r.ffn && r.batch == 1 && !r.out_pre && !sk && r.K % mmk::kSlabK == 0 &&
+        r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31))) {
     c.bm = c.bn = 256;
     c.wgm = c.wgn = 2;
     c.pipe = 3;
@@ -575,6 +582,9 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // the batched form and the pre-activation output run on the slab and
     // basic kernels
     if ((r.batch > 1 || r.out_pre) && (fam == 1 || fam == 2)) continue;
+    // the ping-pong and wave-specialized kernels only under their own
+    // configuration (fam == c.pipe), never as another family's fallback
+    if ((fam == 4 || fam == 5) && fam != c.pipe) continue;
     // the slab kernel runs whole super-steps of 64 k, two of them in flight
     if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
     // its [K][N]-weight and [K][M]-activation forms address a super-step's
@@ -894,7 +904,8 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
               false, form == 1};
     Plan pl;
     if (plan_host(r, c, &pl) == MM_OK)
-      kernel = pl.kernel->pipe == 4   ? "gemm_ws"
+      kernel = pl.kernel->pipe == 5   ? "gemm_pp"
+               : pl.kernel->pipe == 4 ? "gemm_ws"
                : pl.kernel->pipe == 3 ? "gemm_nt_slab"
                : pl.kernel->pipe == 2 ? "gemm_pingpong"
                : pl.kernel->pipe      ? "gemm_nt_pipe"

@@ -218,10 +218,12 @@ mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* 
  * tiles; XCD: XCD-aware workgroup remap on/off; KALT: alternate the K
  * direction per persistent tile (1), never (0) or automatically (2);
  * GRID: persistent grid size, 0 = one wave of resident workgroups; PIPE:
- * preferred kernel family, 4 wave-specialized producer/consumer (with
- * BM=256,BN=128,WM=2,WN=4), 3 whole-line slab ring, 2 ping-pong, 1 32-k
- * pipeline, 0 basic; SK: stream-K chunks per tile when a workspace is
- * given, 0 automatic, 1 never, n >= 2 forced).  The
+ * preferred kernel family, 5 two-group ping-pong over alternate tiles and
+ * 4 wave-specialized producer/consumer (both with BM=256,BN=128,WM=2,WN=4),
+ * 3 whole-line slab ring, 2 split-phase on one tile, 1 32-k pipeline,
+ * 0 basic; SK: stream-K chunks per tile when a workspace is given,
+ * 0 automatic, 1 never, n >= 2 forced; BSTAGE=1: linear forms with a bias
+ * take the slab instance that brings the bias into LDS under the K loop).  The
  * heuristic is replaced for every later call in the process, in the manner
  * of the pages' heuristic plugin (PR "Translate MmaOp patterns properly on
  * Hopper", review of MatmulSchedulerPluginTest).  NULL or "" restores the

@@ -35,6 +35,12 @@ CONFIGS = [
     # small grid so that the ring runs across several tiles per workgroup
     "BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=4",
     "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=4",
+    # two-group ping-pong over alternate 256 x 128 tiles; with a small grid
+    # each workgroup swaps roles across many tiles, its epilogues running in
+    # row blocks (K >= 8 super-steps) or whole (shorter K) under the other
+    # group's K loop
+    "BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=5",
+    "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=5",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
     # the slab instance that brings each tile's bias into LDS under the K
@@ -138,6 +144,20 @@ def test_ws_config_selects_ws_kernel():
             assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_ws")
         assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_pipe")
         assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
+    finally:
+        binding.set_config(None)
+
+
+def test_pp_config_selects_pp_kernel():
+    """PIPE=5 runs the ping-pong kernel where it applies (K-contiguous single
+    weight, whole super-steps) and the default slab tile elsewhere."""
+    binding.set_config("BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=5")
+    try:
+        for (M, N, K) in shapes_for("nt")[-3:]:
+            assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_pp")
+        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_pipe")
+        assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
+        assert binding.describe_config("matmul", 520, 392, 4160, "nn").endswith("KERNEL=gemm_nt_slab")
     finally:
         binding.set_config(None)
 
@@ -862,6 +882,28 @@ def test_bias_staged_workload_mapping(dev):
     cfg = binding.describe_config(w.form, w.M, w.N, w.K, w.layout).rsplit(",KERNEL=", 1)[0] + ",BSTAGE=1"
     binding.set_config(cfg)
     say("bias staged mapping", cfg)
+    ops, kw = mapping_case(w)
+    buf, out = guarded_out(w.M, w.N, False, dev)
+    g = {k: v.to(dev) for k, v in ops.items()}
+    mm.linear(g["A"], g["B"], g["bias"], "bias", out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, w.M, w.N)
+    got = out.cpu()
+    del buf, out, g
+    _, ref_bits = oracle.gemm(**kw)
+    bad = np.argwhere(to_bits(got) != ref_bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["linear_bias_gelu_8192", "linear_bias_gelu_4096"])
+def test_pingpong_workload_mapping(dev, name):
+    """The two-group ping-pong kernel (PIPE=5) at the linear workloads' real
+    shapes: integer operands, bias epilogue, every output bit equal to the
+    oracle's, guard bands intact."""
+    w = synth.WORKLOADS[name]
+    binding.set_config("BM=256,BN=128,WM=2,WN=4,G=4,XCD=1,KALT=0,PIPE=5")
+    assert binding.describe_config(w.form, w.M, w.N, w.K, w.layout).endswith("KERNEL=gemm_pp")
+    say("ping-pong mapping", name)
     ops, kw = mapping_case(w)
     buf, out = guarded_out(w.M, w.N, False, dev)
     g = {k: v.to(dev) for k, v in ops.items()}
