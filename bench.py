@@ -146,7 +146,7 @@ def main() -> int:
     if args.config:
         binding.set_config(args.config)
     name = args.workload or synth.HEADLINE
-    w = synth.WORKLOADS[name]
+    w = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.EXTRA_WORKLOADS[name]
     dev = torch.device("cuda:0")
     host = w.make()
     t = {k: v.to(dev) for k, v in host.items()}

@@ -127,6 +127,18 @@ WORKLOADS: Dict[str, Workload] = {
     ]
 }
 
+# Shapes measured for one design question each (bench.py --workload), not
+# parity workloads: an 8192 x 8192 output (four tiles per workgroup) with
+# K = 65536, whose 32 MiB K panels are far larger than an XCD's 4 MiB L2 --
+# where the direction of each tile's K loop could matter.
+EXTRA_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("matmul_nt_8192x8192x65536", "matmul", 8192, 8192, 65536, "nt", "none", "bf16",
+                 (TensorSpec("A", (8192, 65536), 1.0, 701), TensorSpec("Bt", (8192, 65536), 2.0 ** -8, 702))),
+    ]
+}
+
 # The workload the headline throughput is quoted on.
 HEADLINE = "linear_bias_gelu_8192"
 
