@@ -235,10 +235,11 @@ def main() -> int:
     amk = str(w.layout in ("tn", "tt")).lower()
     if splitk:
         # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights,
-        # [K][M] activations, bias staged in LDS>
-        kernel = (f"mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, {bkn}, {amk}, false> + "
+        # [K][M] activations, bias staged in LDS>; SPLIT=<chunks>x<tile width>
+        chunks, bn = cfg.get("SPLIT", "0x256").split("x")
+        kernel = (f"mmk::gemm_nt_slab<256, {bn}, 2, 2, false, true, false, {bkn}, {amk}, false> + "
                   "mmk::splitk_reduce")
-        tiles = "BM=256,BN=256,WM=2,WN=2,SPLITK,KERNEL=gemm_nt_slab+splitk_reduce"
+        tiles = f"BM=256,BN={bn},WM=2,WN=2,SPLITK={chunks},KERNEL=gemm_nt_slab+splitk_reduce"
     elif cfg["KERNEL"] == "gemm_nt_slab":
         bstage = str(cfg.get("BSTAGE") == "1" and w.form == "linear" and "bias" in w.epilogue
                      and w.layout == "nt").lower()

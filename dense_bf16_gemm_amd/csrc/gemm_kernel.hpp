@@ -111,6 +111,7 @@ struct SkReduceParams {
   int chunks;  // n
   int items;   // q, 0 = chunk-major
   int out_f32, out_vec;
+  int tile_n;  // output columns per tile (256, or 192); slots stay 256 columns wide
 };
 
 // Schedule helpers, shared with the host so that it can describe the order.

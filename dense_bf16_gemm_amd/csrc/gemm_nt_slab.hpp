@@ -86,23 +86,41 @@ __device__ __forceinline__ void gelu_tanh8(float (&v)[8]) {
 // the three free issue slots after each of the row's eight MFMAs.
 // 0x008: MFMA, 0x006: scalar or vector ALU, 0x020: memory read (the copy),
 // 0x100: LDS read.
+// MPR: MFMAs per row (8 for a 128-column wave block, 6 for 96 columns).
+template <int MPR>
 __device__ __forceinline__ void spread_first_row_a() {
+  if constexpr (MPR == 8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);
-  }
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+    }
+  } else {
+    static_assert(MPR == 6, "rows of 8 or 6 MFMAs");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 5, 0);
+    }
   }
   __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 }
+template <int MPR>
 __device__ __forceinline__ void spread_first_row_b() {
+  constexpr int lead = MPR == 8 ? 3 : 2;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < lead; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
   }
@@ -113,12 +131,14 @@ __device__ __forceinline__ void spread_first_row_b() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (MPR == 8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
 }
 
 // Last row of a super-step: 2, 2 and 1 scalar instructions after its first
-// three MFMAs, the row's LDS read after the fourth.
+// three MFMAs, the row's LDS read after the fourth (after the third, with
+// three MFMAs per half row).
+template <int MPR>
 __device__ __forceinline__ void spread_loop_latch() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
@@ -126,7 +146,7 @@ __device__ __forceinline__ void spread_loop_latch() {
   __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (MPR == 8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 }
 
@@ -178,10 +198,14 @@ gemm_nt_slab(GemmParams p) {
   constexpr int FN = WTN / 16;
   constexpr int OUT_BN = FFN ? BN / 2 : BN;
   constexpr int UNIT = 256 * kSlabRowB;  // 32 KiB
-  static_assert(BM == 256 && BN == 256 && NW == 4, "a unit holds 256 rows; four waves");
-  static_assert(FM == 8 && FN == 8, "row schedule assumes 8 x 8 fragments per wave");
-  constexpr int CPS = 256 / 8 / NW;  // 1 KiB copies per wave per slab
-  static_assert(CPS == FM, "one copy per MFMA row");
+  // BN = 192 (a 128 x 96 block per wave): the split-K instance for products
+  // whose 256 x 256 tiles would leave a quarter of the grid idle
+  static_assert(BM == 256 && (BN == 256 || (BN == 192 && SPLITK && !BKN && !AMK)) && NW == 4,
+                "a unit holds 256 rows; four waves");
+  static_assert(FM == 8 && (FN == 8 || FN == 6), "row schedule assumes 8 x 8 (or 8 x 6) fragments per wave");
+  constexpr int CPS = BM / 8 / NW;     // 1 KiB activation copies per wave per slab
+  constexpr int CPS_B = BN / 8 / NW;   // weight copies (as many, or 6 for BN = 192)
+  static_assert(CPS == FM, "one activation copy per MFMA row");
 
   __shared__ __attribute__((aligned(1024))) char smem[kSlabUnits * UNIT];
 
@@ -475,9 +499,9 @@ gemm_nt_slab(GemmParams p) {
 #pragma unroll
       for (int c = 0; c < CPS; ++c) copy_a(c, kbytes, 2 * s);
 #pragma unroll
-      for (int c = 0; c < CPS; ++c) copy_b(c, kbytes, 2 * s + 1);
+      for (int c = 0; c < CPS_B; ++c) copy_b(c, kbytes, 2 * s + 1);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * CPS));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS + CPS_B));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int f = 0; f < FM; ++f) read_a(f, 0, a_x0);
@@ -555,7 +579,7 @@ gemm_nt_slab(GemmParams p) {
       }
       if (r == 0) {
         mfma_half(r, 0, 1);
-        spread_first_row_a();
+        spread_first_row_a<FN>();
       } else {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(r, 0, 1);
@@ -588,7 +612,7 @@ gemm_nt_slab(GemmParams p) {
       const int r = (p + 4) & 7;
       mfma_half(r, 1, 0);
       if (p == 1) copy_b(0, kbytes, cub);
-      copy_b(p, kbytes, cub);
+      if (p < CPS_B) copy_b(p, kbytes, cub);
       if constexpr (BSTAGE)
         if (p == 2) copy_bias(ub);  // five weight copies follow it
       if (p <= FN / 2) {
@@ -597,7 +621,7 @@ gemm_nt_slab(GemmParams p) {
       }
       if (p == 1) {
         mfma_half(r, 1, 1);
-        spread_first_row_b();
+        spread_first_row_b<FN>();
       } else {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(r, 1, 1);
@@ -606,7 +630,7 @@ gemm_nt_slab(GemmParams p) {
         // last row: the loop's own scalar bookkeeping (counter, compare,
         // carried unit) goes between its MFMAs instead of after them
         read_a(r, 0, a_nxt);
-        spread_loop_latch();
+        spread_loop_latch<FN>();
       } else {
         __builtin_amdgcn_sched_barrier(0);
         read_a(r, 0, a_nxt);
@@ -674,7 +698,7 @@ gemm_nt_slab(GemmParams p) {
       // 16-byte chunk 4 pr + lk of the wave's 256 bytes sits in block pr / 2,
       // at physical chunk ((4 pr + lk) & 7) ^ s, s the row-0 swizzle of the
       // copies; five weight copies were issued after it
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS - 3));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(CPS_B - 3));
       const int bunit = cur_unit == 0 ? kSlabUnits - 1 : cur_unit - 1;
       const int bsw = lds_swz(8 * (wave & 2));
       u32x4 w[PAIRS];
@@ -872,8 +896,8 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
     // rows not 16-byte aligned: thread = one column of the 8 rows, so that
     // each load and each store of a wave covers consecutive elements
     const int c = threadIdx.x;
-    const int n = tn * 256 + c;
-    if (n >= p.N) return;
+    const int n = tn * p.tile_n + c;
+    if (c >= p.tile_n || n >= p.N) return;
     float v[8];
     for (int w = s0; w <= s1; w += sstep) {
       const float* src = p.part + (int64_t)slot_of(w) * (256 * 256) + r0 * 256 + c;
@@ -898,8 +922,8 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
   // aligned rows: thread = 8 consecutive columns of one row, 16-byte accesses
   const int r = r0 + (threadIdx.x >> 5);
   const int c = (threadIdx.x & 31) << 3;
-  const int m = tm * 256 + r, n = tn * 256 + c;
-  if (m >= p.M || n >= p.N) return;
+  const int m = tm * 256 + r, n = tn * p.tile_n + c;
+  if (c >= p.tile_n || m >= p.M || n >= p.N) return;
   float v[8];
   for (int w = s0; w <= s1; w += sstep) {
     const f32x4* src = reinterpret_cast<const f32x4*>(p.part + (int64_t)slot_of(w) * (256 * 256) + r * 256 + c);

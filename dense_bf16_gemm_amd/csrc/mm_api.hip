@@ -84,6 +84,14 @@ struct KernelEntry {
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, !(BKC), !(AKC)>), \
    {0}, true}
 
+// split-K pieces on 256 x 192 tiles (K-contiguous operands): for products
+// whose 256 x 256 tiles, split, would leave a quarter or more of the grid idle
+#define MM_KSK192()                                                                        \
+  {256, 192, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, 192, 2, 2, false, true, false, false, false, false>),       \
+   {0}, true}
+
 #define MM_KSP()                                                                           \
   {256, 256, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, true>), {0}, \
@@ -120,6 +128,7 @@ KernelEntry g_kernels[] = {
     MM_KSK(true, false),
     MM_KSK(false, false),
     MM_KSK(false, true),
+    MM_KSK192(),
     MM_KSP(),
     MM_KSB(),
     MM_KWS(),
@@ -488,6 +497,7 @@ struct SkPlan {
   int n = 1;        // chunks per tile (1 = no split)
   int q = 0;        // chunks per workgroup range; 0 = chunk-major, one per workgroup
   int64_t wgs = 0;  // workgroups with work (the grid)
+  int bn = 256;     // tile width: 256, or 192 (K-contiguous operands)
 };
 
 // Chunks and their dealing for `wgs` resident workgroups.  Automatic: only
@@ -499,10 +509,11 @@ struct SkPlan {
 // chunk-major vs 785 us in ranges of 3/8 of a tile; 3584 x 3584 x 16384
 // (196 tiles) 320 us unsplit vs 538 us in ranges of 7/8 of a tile.  Stream-K
 // stays available through a forced chunk count (SK=n with n T > wgs).
-SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
+SkPlan splitk_plan_bn(const Request& r, const Config& c, int64_t wgs, int bn) {
   SkPlan sp;
+  sp.bn = bn;
   if (c.sk == 1 || !splitk_shape(r) || wgs > kSkMaxWgs) return sp;
-  const int64_t T = cdiv(r.M, 256) * cdiv(r.N, 256);
+  const int64_t T = cdiv(r.M, 256) * cdiv(r.N, bn);
   const int64_t KS = r.K / mmk::kSlabK;
   int n;
   if (c.sk >= 2) {
@@ -535,6 +546,18 @@ SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
   return sp;
 }
 
+// The automatic split takes 256 x 192 tiles (K-contiguous operands) when they
+// occupy more of the grid than 256 x 256 tiles: the 2047 x 3001 x 65536 fp32
+// matmul has 96 tiles of 256 x 256 (2 chunks each: 192 of 256 workgroups) or
+// 128 of 256 x 192 (2 chunks: all 256).  A forced configuration keeps 256.
+SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
+  SkPlan a = splitk_plan_bn(r, c, wgs, 256);
+  if (c.forced || !(a_kcontig(r.layout) && b_kcontig(r.layout))) return a;
+  SkPlan b = splitk_plan_bn(r, c, wgs, 192);
+  if (b.n > 1 && b.q == 0 && (a.n <= 1 || (a.q == 0 && b.wgs > a.wgs))) return b;
+  return a;
+}
+
 // one slot per chunk-major workgroup; two per stream-K workgroup (its range
 // may end one tile and start the next)
 int64_t splitk_ws_bytes(const SkPlan& sp) {
@@ -560,9 +583,10 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   Config c = c_in;
   KernelEntry* k = nullptr;
   if (sk) {
-    c.bm = c.bn = 256;
+    c.bm = 256;
+    c.bn = sp.bn;
     c.wgm = c.wgn = 2;
-    k = find_kernel(256, 256, 2, 2, a_kc, b_kc, false, 3, true);
+    k = find_kernel(256, sp.bn, 2, 2, a_kc, b_kc, false, 3, true);
   }
   // the wave-specialized kernel (a configuration override for comparison)
   // takes single-weight K-contiguous products with whole super-steps; other
@@ -713,6 +737,7 @@ mm_status run(const Request& r, void* stream) {
     rp.items = sp.q;
     rp.out_f32 = pl.p.out_f32;
     rp.out_vec = pl.p.out_vec;
+    rp.tile_n = sp.bn;
     void* rargs[] = {&rp};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::splitk_reduce), dim3((unsigned)(32 * rp.num_tiles)),
                         dim3(256), rargs, 0, static_cast<hipStream_t>(stream));
@@ -912,10 +937,25 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
                                       : "gemm_persistent";
     g_last_error.clear();
   }
+  // a plain product that a workspace would split: chunks per tile and tile
+  // width on the current device (queries the device; left out without one)
+  char split[32] = "";
+  if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
+    Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
+              false, false};
+    int cus = 0, occ = 0;
+    if (splitk_shape(r) && device_cus(&cus) == MM_OK &&
+        kernel_occupancy(find_kernel(256, 256, 2, 2, a_kcontig(r.layout), b_kcontig(r.layout), false, 3, true),
+                         &occ) == MM_OK) {
+      const SkPlan sp = splitk_plan(r, c, splitk_wgs(c, cus, occ));
+      if (sp.n > 1) std::snprintf(split, sizeof split, ",SPLIT=%dx%d", sp.n, sp.bn);
+    }
+    g_last_error.clear();
+  }
   std::snprintf(buf, (size_t)buflen,
-                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,%sKERNEL=%s", c.bm, c.bn,
+                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,%sKERNEL=%s%s", c.bm, c.bn,
                 c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe,
-                c.bstage ? "BSTAGE=1," : "", kernel);
+                c.bstage ? "BSTAGE=1," : "", kernel, split);
   return MM_OK;
 }
 

@@ -915,3 +915,20 @@ def test_pingpong_workload_mapping(dev, name):
     _, ref_bits = oracle.gemm(**kw)
     bad = np.argwhere(to_bits(got) != ref_bits)
     assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def test_splitk_tile_width_choice(dev):
+    """The automatic split takes 256 x 192 tiles when they occupy more of the
+    grid: the long-K workload's 128 such tiles in 2 chunks fill all 256 CUs
+    (256 x 256 tiles: 96 in 2 chunks, 192 workgroups); a forced configuration
+    and operands not stored K-contiguous keep 256 x 256."""
+    if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
+        pytest.skip("the choice is stated for a 256-CU GPU")
+    assert binding.describe_config("matmul", 2047, 3001, 65536).endswith("SPLIT=2x192")
+    assert binding.describe_config("matmul", 2047, 3001, 65536, "nn").endswith("SPLIT=2x256")
+    binding.set_config("BM=256,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=2,PIPE=3")
+    try:
+        assert binding.describe_config("matmul", 2047, 3001, 65536).endswith("SPLIT=2x256")
+    finally:
+        binding.set_config(None)
+    assert "SPLIT" not in binding.describe_config("matmul", 8192, 8192, 8192)
