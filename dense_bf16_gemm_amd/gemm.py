@@ -58,6 +58,21 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     return ws
 
 
+def release_workspaces(device=None) -> None:
+    """Drops the cached split-K workspaces (all devices, or one), so their
+    memory returns to torch's caching allocator.  Call it after the work of
+    every stream that used them has been synchronized; later split-K calls
+    allocate a new one on demand."""
+    if device is None:
+        _workspaces.clear()
+        return
+    index = torch.device(device).index
+    if index is None:
+        index = torch.cuda.current_device()
+    for key in [k for k in _workspaces if k[0] == index]:
+        del _workspaces[key]
+
+
 def _resolve_ws(workspace, form: str, M: int, N: int, K: int, layout: str, device):
     """(pointer, bytes) of the split-K workspace: "auto" uses the current
     stream's cached one, sized by mm_workspace_size; None disables split-K; a

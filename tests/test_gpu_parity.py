@@ -481,8 +481,9 @@ def test_splitk_auto_workspace_two_streams(dev):
             for out in got:
                 np.testing.assert_array_equal(to_bits(out), bits)
     finally:
-        for k in keys:
-            gemm_mod._workspaces.pop(k, None)
+        torch.cuda.synchronize()
+        mm.release_workspaces(dev)
+        assert not any(k[0] == dev.index for k in gemm_mod._workspaces)
 
 
 def test_splitk_random_and_fallbacks(dev):
