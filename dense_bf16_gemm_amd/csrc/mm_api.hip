@@ -948,14 +948,14 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
         kernel_occupancy(find_kernel(256, 256, 2, 2, a_kcontig(r.layout), b_kcontig(r.layout), false, 3, true),
                          &occ) == MM_OK) {
       const SkPlan sp = splitk_plan(r, c, splitk_wgs(c, cus, occ));
-      if (sp.n > 1) std::snprintf(split, sizeof split, ",SPLIT=%dx%d", sp.n, sp.bn);
+      if (sp.n > 1) std::snprintf(split, sizeof split, "SPLIT=%dx%d,", sp.n, sp.bn);
     }
     g_last_error.clear();
   }
   std::snprintf(buf, (size_t)buflen,
-                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,%sKERNEL=%s%s", c.bm, c.bn,
+                "BM=%d,BN=%d,WM=%d,WN=%d,G=%d,XCD=%d,KALT=%d,GRID=%d,PIPE=%d,%s%sKERNEL=%s", c.bm, c.bn,
                 c.wgm, c.wgn, c.group, c.xcd, k_alt_enabled(c, K) ? 1 : 0, c.grid, c.pipe,
-                c.bstage ? "BSTAGE=1," : "", kernel, split);
+                c.bstage ? "BSTAGE=1," : "", split, kernel);
   return MM_OK;
 }
 

@@ -234,10 +234,10 @@ mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* 
 mm_status mm_set_config(const char* spec);
 
 /* Describes the configuration the next call of this shape would use, for
- * logging and tests: writes a string like the one mm_set_config accepts,
- * then KERNEL=<family>, and for a plain product that a split-K workspace
- * would split on the current device, SPLIT=<chunks per tile>x<tile width>
- * (that part queries the device and is left out when there is none).
+ * logging and tests: writes a string like the one mm_set_config accepts;
+ * for a plain product that a split-K workspace would split on the current
+ * device, SPLIT=<chunks per tile>x<tile width> (that part queries the device
+ * and is left out when there is none); and last KERNEL=<family>.
  * form: 0 matmul/linear, 1 FFN. Returns MM_ERR_INVALID_VALUE for bad args. */
 mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
                              char* buf, int64_t buflen);
