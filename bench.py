@@ -32,7 +32,6 @@ import os
 import re
 import statistics
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -75,43 +74,23 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-class ClockSampler(threading.Thread):
-    """Samples the GPU's current GFX clock from the driver's sysfs table (the
-    starred line of pp_dpm_sclk) about every half millisecond while running.
-    Only when exactly one card exposes the table (a one-GPU machine); else no
-    samples are taken."""
+def sclk_path():
+    """The driver's GFX clock table (pp_dpm_sclk; its starred line is the
+    current clock) when exactly one card exposes one (a one-GPU machine)."""
+    paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+    return paths[0] if len(paths) == 1 else None
 
-    def __init__(self):
-        super().__init__(daemon=True)
-        paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
-        self.path = paths[0] if len(paths) == 1 else None
-        self.samples = []
-        self.stop_flag = threading.Event()
 
-    def read(self):
-        try:
-            with open(self.path) as f:
-                for line in f:
-                    if line.rstrip().endswith("*"):
-                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
-                        return int(m.group(1)) if m else None
-        except OSError:
-            return None
+def read_sclk(path):
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    return int(m.group(1)) if m else None
+    except OSError:
         return None
-
-    def run(self):
-        while self.path and not self.stop_flag.is_set():
-            v = self.read()
-            if v is not None:
-                self.samples.append(v)
-            time.sleep(0.0005)
-
-    def summary(self):
-        if not self.samples:
-            return None
-        return {"median": statistics.median(self.samples), "min": min(self.samples),
-                "max": max(self.samples), "samples": len(self.samples),
-                "source": "pp_dpm_sclk (current level), sampled over the timed region"}
+    return None
 
 
 def cpu_baseline(w, tensors, target_s: float):
@@ -239,8 +218,7 @@ def main() -> int:
     # Timed region: the K steps back to back, with one event pair around all
     # of them (events between launches would add their own gaps to it).
     torch.cuda.synchronize()
-    sampler = ClockSampler()
-    sampler.start()
+    clock_path = sclk_path()
     t0 = time.perf_counter()
     whole0 = torch.cuda.Event(enable_timing=True)
     whole1 = torch.cuda.Event(enable_timing=True)
@@ -248,10 +226,17 @@ def main() -> int:
     for _ in range(args.steps):
         step()
     whole1.record(stream)
+    # while the GPU works through the timed launches, this thread (no other)
+    # samples the clock every millisecond; a step bound by the host's launch
+    # rate leaves little to wait for and gets few samples
+    sclk = []
+    while clock_path and not whole1.query():
+        v = read_sclk(clock_path)
+        if v is not None:
+            sclk.append(v)
+        time.sleep(0.001)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sampler.stop_flag.set()
-    sampler.join()
     ms_total = whole0.elapsed_time(whole1)
     # Then the same number of launches again, each between its own events, for
     # the kernel's mean launch duration (the roofline figure).
@@ -304,7 +289,10 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "settle": settle,
-        "sclk_mhz": sampler.summary(),
+        "sclk_mhz": ({"median": statistics.median(sclk), "min": min(sclk), "max": max(sclk),
+                      "samples": len(sclk),
+                      "source": "pp_dpm_sclk (current level) while the timed launches ran"}
+                     if sclk else None),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
