@@ -114,6 +114,17 @@ struct SkReduceParams {
   int tile_n;  // output columns per tile (256, or 192); slots stay 256 columns wide
 };
 
+// A product with K = 0 (empty_k_fill): every sum over k is empty.
+struct EmptyKParams {
+  const uint16_t* bias;  // read only when epi adds a bias
+  void* out;
+  void* out_pre;        // the pre-activation output, or null
+  int64_t M, N, batch;
+  int64_t stride_out;   // elements between batch entries of out
+  int epi;              // EPI_*; the gated FFN forms pass EPI_NONE
+  int out_f32;
+};
+
 // Schedule helpers, shared with the host so that it can describe the order.
 __host__ __device__ inline int remap_workgroup(int b, int G, int on) {
   if (!on || G < kNumXcd) return b;
@@ -573,6 +584,31 @@ gemm_persistent(GemmParams p) {
       if (has_next) store_staged((it + 1) & 1);
     }
     epilogue(tile_i);
+  }
+}
+
+// K = 0: the sum over k of each output is empty, i.e. 0, so the output is
+// the epilogue applied to 0 + bias[n] (GELU(bias[n]), bias[n] or 0), rounded
+// once; the gated FFN forms give act(0) * 0 = 0.  One element per thread,
+// batch entries and rows in order.
+__global__ void __launch_bounds__(256) empty_k_fill(EmptyKParams p) {
+  const int64_t per = p.M * p.N;
+  const int64_t total = per * p.batch;
+  const bool add_bias = p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU;
+  const bool act = p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / per;
+    const int64_t e = i - b * per;
+    const int64_t o = b * p.stride_out + e;
+    const float t = add_bias ? __builtin_bit_cast(float, (uint32_t)p.bias[e % p.N] << 16) : 0.0f;
+    const float y = act ? gelu_tanh(t) : t;
+    if (p.out_f32) {
+      static_cast<float*>(p.out)[o] = y;
+      if (p.out_pre) static_cast<float*>(p.out_pre)[o] = t;
+    } else {
+      static_cast<uint16_t*>(p.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y));
+      if (p.out_pre) static_cast<uint16_t*>(p.out_pre)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(t));
+    }
   }
 }
 

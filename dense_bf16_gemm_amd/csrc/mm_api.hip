@@ -11,6 +11,7 @@
 // default heuristic (same PR, review of MatmulSchedulerPluginTest).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -410,30 +411,38 @@ mm_status validate(const Request& r) {
     return fail(MM_ERR_UNSUPPORTED, "M, N and K must be below 2^31");
   if (r.layout < MM_NN || r.layout > MM_TT) return fail(MM_ERR_INVALID_VALUE, "bad layout");
   if (r.M == 0 || r.N == 0) return MM_OK;
-  if (r.K == 0) return fail(MM_ERR_UNSUPPORTED, "K == 0 is not supported");
-  if (!r.A || !r.B || !r.out) return fail(MM_ERR_INVALID_VALUE, "null operand pointer");
-  if (r.ffn && !r.B2) return fail(MM_ERR_INVALID_VALUE, "null W_up pointer");
+  // K == 0: the operands hold no elements and are never read (they may be
+  // null); the output is the epilogue of an empty sum (empty_k_fill)
+  const bool reads = r.K > 0;
+  if (!r.out || (reads && (!r.A || !r.B))) return fail(MM_ERR_INVALID_VALUE, "null operand pointer");
+  if (reads && r.ffn && !r.B2) return fail(MM_ERR_INVALID_VALUE, "null W_up pointer");
   const bool need_bias = (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
   if (need_bias && !r.bias) return fail(MM_ERR_INVALID_VALUE, "epilogue needs a bias");
   const bool a_kc = (r.layout == MM_NN || r.layout == MM_NT);
   const bool b_kc = (r.layout == MM_NT || r.layout == MM_TT);
-  if (!aligned(r.A, 16) || !aligned(r.B, 16) || (r.ffn && !aligned(r.B2, 16)))
+  if (reads && (!aligned(r.A, 16) || !aligned(r.B, 16) || (r.ffn && !aligned(r.B2, 16))))
     return fail(MM_ERR_MISALIGNED, "operand pointers must be 16-byte aligned");
   if (r.batch > 1) {
-    if (r.stride_a % 8 != 0 || r.stride_b % 8 != 0)
+    if (reads && (r.stride_a % 8 != 0 || r.stride_b % 8 != 0))
       return fail(MM_ERR_MISALIGNED, "operand batch strides must be multiples of 8 elements");
     if (r.stride_out < r.M * r.N)
       return fail(MM_ERR_INVALID_VALUE, "output batch stride smaller than M * N: entries would overlap");
   }
-  if ((a_kc ? r.K : r.M) % 8 != 0)
+  if (reads && (a_kc ? r.K : r.M) % 8 != 0)
     return fail(MM_ERR_MISALIGNED, "the contiguous extent of A must be a multiple of 8 elements");
-  if ((b_kc ? r.K : r.N) % 8 != 0)
+  if (reads && (b_kc ? r.K : r.N) % 8 != 0)
     return fail(MM_ERR_MISALIGNED, "the contiguous extent of B must be a multiple of 8 elements");
   if (need_bias && !aligned(r.bias, 2)) return fail(MM_ERR_MISALIGNED, "bias must be 2-byte aligned");
   const int esize = r.out_f32 ? 4 : 2;
   if (!aligned(r.out, esize)) return fail(MM_ERR_MISALIGNED, "out must be aligned to its element size");
-  // byte extents over every batch entry
+  // every extent (over all batch entries) below 2^60 elements, so that the
+  // byte counts below cannot overflow
   const int64_t nb = r.batch - 1;
+  const int64_t room = int64_t(1) << 60;
+  auto fits = [&](int64_t stride, int64_t one) { return one <= room && (nb == 0 || stride <= (room - one) / nb); };
+  if (!fits(r.stride_a, r.M * r.K) || !fits(r.stride_b, r.K * r.N) || !fits(r.stride_out, r.M * r.N))
+    return fail(MM_ERR_UNSUPPORTED, "an operand or the output spans 2^60 elements or more");
+  // byte extents over every batch entry
   const int64_t ob = (nb * r.stride_out + r.M * r.N) * esize;
   const int64_t ab = (nb * r.stride_a + r.M * r.K) * 2, bb = (nb * r.stride_b + r.K * r.N) * 2;
   if (overlaps(r.out, ob, r.A, ab) || overlaps(r.out, ob, r.B, bb) ||
@@ -676,10 +685,31 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   return MM_OK;
 }
 
+// K == 0: one launch of empty_k_fill over every output element
+mm_status run_empty_k(const Request& r, void* stream) {
+  mmk::EmptyKParams p;
+  p.bias = static_cast<const uint16_t*>(r.bias);
+  p.out = r.out;
+  p.out_pre = r.out_pre;
+  p.M = r.M;
+  p.N = r.N;
+  p.batch = r.batch;
+  p.stride_out = r.batch > 1 ? r.stride_out : r.M * r.N;
+  p.epi = r.ffn ? mmk::EPI_NONE : r.epi;
+  p.out_f32 = r.out_f32 ? 1 : 0;
+  const int64_t blocks = std::min<int64_t>(cdiv(r.M * r.N * r.batch, 256), 8192);
+  void* args[] = {&p};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::empty_k_fill), dim3((unsigned)blocks),
+                                       dim3(256), args, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel (K = 0): ") + hipGetErrorString(e));
+  return MM_OK;
+}
+
 mm_status run(const Request& r, void* stream) {
   mm_status s = validate(r);
   if (s != MM_OK) return s;
   if (r.M == 0 || r.N == 0) return MM_OK;
+  if (r.K == 0) return run_empty_k(r, stream);
   const Config c = choose_config(r.ffn, r.M, r.N, r.K);
   Plan pl;
   SkPlan sp;
@@ -923,7 +953,7 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
     return fail(MM_ERR_INVALID_VALUE, "bad arguments");
   const Config c = choose_config(form == 1, M, N, K);
   // the kernel a call of this shape would launch (no HIP call is made)
-  const char* kernel = "none";
+  const char* kernel = M > 0 && N > 0 && K == 0 ? "empty_k_fill" : "none";
   if (M > 0 && N > 0 && K > 0) {
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
               false, form == 1};

@@ -17,23 +17,27 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
  *     never allocates, frees or keeps a pointer past the return of a call.
- *   - Each successful call with M > 0 and N > 0 enqueues exactly ONE kernel on
- *     `stream` (a hipStream_t; NULL means the default stream) and returns
- *     without synchronizing.  Errors in execution surface on the stream.
+ *   - Each successful call with M > 0 and N > 0 enqueues its work on `stream`
+ *     (a hipStream_t; NULL means the default stream): one kernel, or two for a
+ *     split-K call (the pieces, then their reduction), and returns without
+ *     synchronizing.  Errors in execution surface on the stream.
  *   - Matrices are dense and row-major in their stored shape (the last
  *     dimension is contiguous); a transposed operand is described by the
  *     layout letters, never copied.
  *   - Argument errors are detected on the host before any HIP call, return a
  *     status and have no side effects; mm_last_error() then describes them.
- *   - M == 0 or N == 0 is a successful no-op.  K == 0 is rejected with
- *     MM_ERR_UNSUPPORTED (an empty sum is not a supported use).
+ *   - M == 0 or N == 0 is a successful no-op.  K == 0 is the empty sum: every
+ *     accumulator is 0, so the output is the epilogue of 0 (+ bias): bias[n],
+ *     gelu(bias[n]) or 0, and 0 for the FFN forms (act(0) * 0); the operands
+ *     are then never read and may be null.
  *   - Alignment: A, B (and W_gate/W_up) must be 16-byte aligned and the
  *     contiguous extent of each of them a multiple of 8 elements; bias must be
  *     2-byte aligned; out must be aligned to its element size.  Otherwise
  *     MM_ERR_MISALIGNED.  (The output may have any N, e.g. N = 3001.)
  *   - `out` must not overlap any input (MM_ERR_INVALID_VALUE).
- *   - Sizes: 0 <= M, N < 2^31 and 1 <= K < 2^31; individual operands may hold
- *     more than 2^31 elements (addresses are formed in 64 bits).
+ *   - Sizes: 0 <= M, N, K < 2^31; individual operands may hold more than 2^31
+ *     elements (addresses are formed in 64 bits), each below 2^60 over all
+ *     batch entries (else MM_ERR_UNSUPPORTED).
  *   - Thread safety: calls may be made from several host threads; the only
  *     process-wide state is a per-device attribute cache, the configuration
  *     override (mm_set_config), the thread-local last-error string and the
@@ -237,8 +241,12 @@ mm_status mm_set_config(const char* spec);
  * logging and tests: writes a string like the one mm_set_config accepts;
  * for a plain product that a split-K workspace would split on the current
  * device, SPLIT=<chunks per tile>x<tile width> (that part queries the device
- * and is left out when there is none); and last KERNEL=<family>.
- * form: 0 matmul/linear, 1 FFN. Returns MM_ERR_INVALID_VALUE for bad args. */
+ * and is left out when there is none); and last KERNEL=<family>.  The tile
+ * and KERNEL parts describe a call without a workspace; with SPLIT present,
+ * a call given a workspace (mm_matmul_ws, mm_linear_ws, mm_matmul_noalloc)
+ * runs the slab kernel on 256 x <tile width> tiles instead.  K = 0 names
+ * empty_k_fill.  form: 0 matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE
+ * for bad args. */
 mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
                              char* buf, int64_t buflen);
 

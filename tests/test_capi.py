@@ -71,8 +71,11 @@ def test_argument_errors_return_before_any_device_call(lib):
     assert mm(lib, K=-5) == E.MM_ERR_INVALID_VALUE
     assert mm(lib, layout=7) == E.MM_ERR_INVALID_VALUE
     assert mm(lib, out_dtype=3) == E.MM_ERR_INVALID_VALUE
-    assert mm(lib, K=0) == E.MM_ERR_UNSUPPORTED
-    assert "K == 0" in lib.mm_last_error().decode()
+    # K == 0 is the empty sum: its operands may be null, never its output
+    assert mm(lib, K=0, A=None, B=None, out=None) == E.MM_ERR_INVALID_VALUE
+    assert mm(lib, K=0, A=None, B=None) not in (E.MM_ERR_INVALID_VALUE, E.MM_ERR_UNSUPPORTED,
+                                                 E.MM_ERR_MISALIGNED)
+    assert lin(lib, K=0, x=None, W=None, bias=None, epi=1) == E.MM_ERR_INVALID_VALUE  # bias still needed
     assert mm(lib, M=1 << 31) == E.MM_ERR_UNSUPPORTED
     # alignment of operand pointers and of contiguous extents
     assert mm(lib, A=PA + 2) == E.MM_ERR_MISALIGNED
@@ -194,6 +197,8 @@ def test_batched_argument_checks():
         (2, -8, 0, M * N, binding.MM_ERR_INVALID_VALUE),         # negative stride
         (2, 12, 0, M * N, binding.MM_ERR_MISALIGNED),            # stride not a multiple of 8
         (2, M * K, K * N, M * N - 1, binding.MM_ERR_INVALID_VALUE),  # output entries overlap
+        (2, 1 << 60, 0, M * N, binding.MM_ERR_UNSUPPORTED),      # A spans 2^60 elements
+        (3, 0, 0, 1 << 59, binding.MM_ERR_UNSUPPORTED),          # so does the output
     ]
     for batch, sa, sb, so, want in cases:
         st = lib.mm_matmul_batched(A, B, out, batch, M, N, K, sa, sb, so, binding.LAYOUTS["nt"], 0, None)

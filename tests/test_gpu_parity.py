@@ -740,6 +740,64 @@ def test_empty_and_tiny(dev):
     assert tol_excess(got.cpu().numpy(), y, 1e-3) <= 0
 
 
+def test_empty_sum_k0(dev):
+    """K = 0: every accumulator is the empty sum 0, so each form's output is
+    its epilogue applied to 0 + bias, which the oracle's loop with no k terms
+    gives too: bias exactly, GELU(bias) within the GELU tolerance, zeros for
+    the plain and FFN products.  Operands are empty (null pointers through
+    the C ABI); outputs start as 0xFF bytes, so every element must be
+    written."""
+    M, N = 37, 300
+    say("K = 0", (M, N))
+    bias = synth.randn_bf16((N,), 1.0, 91)
+    bias_d = bias.to(dev)
+    Ah, Bh = np.zeros((M, 0), np.uint16), np.zeros((N, 0), np.uint16)
+    lib = binding.load()
+    for f32 in (False, True):
+        out = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device=dev)
+        out.view(torch.uint8).fill_(0xFF)
+        binding.check(lib.mm_matmul(None, None, out.data_ptr(), M, N, 0, binding.LAYOUTS["nn"],
+                                    1 if f32 else 0, stream()), "mm_matmul")
+        assert torch.all(out == 0)
+    for epi in ("none", "bias", "gelu_tanh", "bias_gelu_tanh"):
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out.view(torch.uint8).fill_(0xFF)
+        b = bias_d if "bias" in epi else None
+        binding.check(lib.mm_linear(None, None, b.data_ptr() if b is not None else None, out.data_ptr(),
+                                    M, N, 0, binding.LAYOUTS["nt"], binding.EPILOGUES[epi], stream()),
+                      "mm_linear")
+        y, bits = oracle.gemm(Ah, Bh, "nt", epi, bias=synth.bits(bias) if b is not None else None)
+        if "gelu" in epi:
+            assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0, epi
+        else:
+            np.testing.assert_array_equal(to_bits(out), bits, err_msg=epi)
+    # the two-output form: the pre-activation is the bias itself
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    pre = torch.empty_like(out)
+    call_linear_preact(torch.empty((M, 0), dtype=torch.bfloat16, device=dev),
+                       torch.empty((N, 0), dtype=torch.bfloat16, device=dev), bias_d, M, N, 0, "nt",
+                       "bias_gelu_tanh", out, pre)
+    y, _ = oracle.gemm(Ah, Bh, "nt", "bias_gelu_tanh", bias=synth.bits(bias))
+    np.testing.assert_array_equal(to_bits(pre), np.broadcast_to(synth.bits(bias), (M, N)))
+    assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0
+    # FFN forms: act(0) * 0 = 0
+    for act in ("silu", "identity"):
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out.view(torch.uint8).fill_(0xFF)
+        binding.check(lib.mm_ffn_glu(None, None, None, out.data_ptr(), M, N, 0, binding.GLU_ACTS[act],
+                                     stream()), "mm_ffn_glu")
+        assert torch.all(out == 0), act
+    # batched with a shared bias, and through the torch-facing wrappers
+    x3 = torch.empty((3, M, 0), dtype=torch.bfloat16, device=dev)
+    got = mm.linear_batched(x3, torch.empty((N, 0), dtype=torch.bfloat16, device=dev), bias_d, "bias")
+    for e in range(3):
+        np.testing.assert_array_equal(to_bits(got[e]), np.broadcast_to(synth.bits(bias), (M, N)))
+    got = mm.matmul(torch.empty((M, 0), dtype=torch.bfloat16, device=dev),
+                    torch.empty((0, N), dtype=torch.bfloat16, device=dev), torch.float32)
+    torch.cuda.synchronize()
+    assert got.shape == (M, N) and torch.all(got == 0)
+
+
 def test_unaligned_output_rows_and_pointer(dev):
     """fp32 rows of 3001 elements (12004 bytes, not 16-byte multiples) and a
     bf16 output that starts 2 bytes past a 16-byte boundary."""

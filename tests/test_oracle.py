@@ -368,3 +368,23 @@ def test_empty_inputs():
     assert y.shape == (0, 5)
     y, _ = oracle.gemm(np.zeros((3, 0), np.uint16), np.zeros((0, 5), np.uint16), "nn")
     assert np.all(y == 0)
+
+
+def test_empty_sum_gives_the_epilogue_of_the_bias():
+    """K = 0: each accumulator is the empty sum 0, so the bias epilogue
+    returns the bias itself (its bf16 bits unchanged), GELU(bias) equals the
+    oracle's GELU of those values, and the gated FFN gives act(0) * 0 = 0."""
+    M, N = 5, 64
+    bias = rand_bits((N,), 83)
+    A, B = np.zeros((M, 0), np.uint16), np.zeros((N, 0), np.uint16)
+    y, bits = oracle.gemm(A, B, "nt", "bias", bias=bias)
+    np.testing.assert_array_equal(bits, np.broadcast_to(bias, (M, N)))
+    np.testing.assert_array_equal(y, np.broadcast_to(bits_to_f32(bias), (M, N)))
+    y, _ = oracle.gemm(A, B, "nt", "bias_gelu_tanh", bias=bias)
+    np.testing.assert_array_equal(y, np.broadcast_to(oracle.gelu_tanh(bits_to_f32(bias)), (M, N)))
+    for epi in ("none", "gelu_tanh"):
+        y, bits = oracle.gemm(A, B, "nt", epi)
+        assert np.all(y == 0) and np.all(bits == 0)
+    for epi in ("swiglu", "glu_identity"):
+        y, _ = oracle.gemm(A, B, "nt", epi, B2=B)
+        assert np.all(y == 0)
