@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the bf16 GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME] [--graph]
 
 A step is one call of the fused operation on one batch of synthetic input
 already resident in device memory (default: linear + bias + GELU(tanh) at
@@ -21,6 +21,12 @@ when they are fewer, by more untimed launches until at least SETTLE_LAUNCHES
 launches and SETTLE_SECONDS of launches have run; the JSON line reports that
 settle phase ("settle": its extra launches, its length, and the mean launch
 time of its first and last windows) beside "warmup".
+
+Launch-bound workloads.  An eager step is a Python call (argument checks, a
+ctypes call) of about 10 us, longer than the 256^3 kernel itself, so eager
+steps measure the host.  --graph captures the K steps into one HIP graph
+and times a replay of it ("launch": "hip_graph" in the JSON line); the
+per-launch figure is then a second replay's time per step.
 """
 from __future__ import annotations
 
@@ -47,9 +53,9 @@ SETTLE_WINDOW = 20
 CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 
-# the headers the slab kernel (every benchmarked workload's kernel) is built
-# from, and the host code that chooses its tile order and launch
-SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp", "mm_api.hip")
+# the headers the benchmarked workloads' kernels are built from, and the host
+# code that chooses their tile order and launch
+SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp", "gemm_small.hpp", "mm_api.hip")
 
 
 def kernel_source_hash() -> str:
@@ -136,6 +142,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--config", default=None, help="tile configuration override (mm_set_config)")
+    ap.add_argument("--graph", action="store_true",
+                    help="issue the timed steps as one captured HIP graph (for launch-bound "
+                         "workloads, whose eager steps measure the host's launch rate)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES bytes (the reference "
                          "kernel for scaling HBM byte counters) and exit")
@@ -184,6 +193,17 @@ def main() -> int:
         step = lambda: mm.ffn_swiglu(t["x"], t["W_gate"], t["W_up"], out=out)  # noqa: E731
 
     stream = torch.cuda.current_stream()  # the stream every launch goes to
+    # --graph: the K steps are captured into a HIP graph before the warm-up
+    # (capturing runs nothing, but takes long enough for the clock to drop)
+    graph = None
+    if args.graph:
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
     settle_t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
@@ -216,15 +236,19 @@ def main() -> int:
         "last_window_us": round(windows[-1], 1) if windows else None,
     }
     # Timed region: the K steps back to back, with one event pair around all
-    # of them (events between launches would add their own gaps to it).
+    # of them (events between launches would add their own gaps to it).  With
+    # --graph the timed region is one replay of the captured steps.
     torch.cuda.synchronize()
     clock_path = sclk_path()
     t0 = time.perf_counter()
     whole0 = torch.cuda.Event(enable_timing=True)
     whole1 = torch.cuda.Event(enable_timing=True)
     whole0.record(stream)
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     whole1.record(stream)
     # while the GPU works through the timed launches, this thread (no other)
     # samples the clock every millisecond; a step bound by the host's launch
@@ -239,15 +263,26 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_total = whole0.elapsed_time(whole1)
     # Then the same number of launches again, each between its own events, for
-    # the kernel's mean launch duration (the roofline figure).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
+    # the kernel's mean launch duration (the roofline figure).  A graph's
+    # launches cannot be bracketed one by one: there the figure is a second
+    # replay's mean time per step, gaps between its launches included.
+    if graph is not None:
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        graph.replay()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        per_launch = [r0.elapsed_time(r1) / args.steps]
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
     ms_per_step = ms_total / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     mean_launch = statistics.fmean(per_launch)
@@ -276,6 +311,9 @@ def main() -> int:
                      and w.layout == "nt").lower()
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
                   f"false, false, {bkn}, {amk}, {bstage}>")
+    elif cfg["KERNEL"] == "gemm_small":
+        kernel = (f"mmk::gemm_small<{str(w.layout in ('nn', 'nt')).lower()}, "
+                  f"{str(w.layout in ('nt', 'tt')).lower()}>")
     elif cfg["KERNEL"] in ("gemm_ws", "gemm_pp"):
         kernel = f"mmk::{cfg['KERNEL']}"
     else:
@@ -288,6 +326,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "launch": "hip_graph" if graph is not None else "stream",
         "settle": settle,
         "sclk_mhz": ({"median": statistics.median(sclk), "min": min(sclk), "max": max(sclk),
                       "samples": len(sclk),

@@ -26,6 +26,7 @@
 #include "gemm_ws.hpp"
 #include "gemm_pp.hpp"
 #include "gemm_nt_slab.hpp"
+#include "gemm_small.hpp"
 
 // Split-K partial tiles of mm_matmul_noalloc: a fixed device array instead of
 // a caller's workspace, for callers that cannot allocate.  64 MiB = one
@@ -52,7 +53,8 @@ mm_status fail(mm_status s, const std::string& msg) {
 struct KernelEntry {
   int bm, bn, wgm, wgn;
   bool a_kc, b_kc, ffn;
-  int pipe;  // 5: two-group ping-pong (gemm_pp), 4: wave-specialized (gemm_ws),
+  int pipe;  // 6: 64 x 64 tiles with all of K in LDS (gemm_small),
+             // 5: two-group ping-pong (gemm_pp), 4: wave-specialized (gemm_ws),
              // 3: whole-line slab ring (gemm_nt_slab),
              // 2: ping-pong (gemm_pingpong),
              // 1: K-contiguous pipeline (gemm_nt_pipe), 0: gemm_persistent
@@ -117,6 +119,9 @@ struct KernelEntry {
 #define MM_KPPT()                                                                          \
   {256, 128, 2, 4, true, true, false, 5, reinterpret_cast<const void*>(&mmk::gemm_pp), {0}}
 
+#define MM_KSM(AKC, BKC)                                                                   \
+  {64, 64, 2, 2, AKC, BKC, false, 6, reinterpret_cast<const void*>(&mmk::gemm_small<AKC, BKC>), {0}}
+
 #define MM_K_LAYOUTS(BM, BN, WGM, WGN)                                                      \
   MM_K(BM, BN, WGM, WGN, true, false, false), MM_K(BM, BN, WGM, WGN, true, true, false),   \
       MM_K(BM, BN, WGM, WGN, false, false, false), MM_K(BM, BN, WGM, WGN, false, true, false)
@@ -150,6 +155,10 @@ KernelEntry g_kernels[] = {
     MM_K_LAYOUTS(256, 256, 2, 2),
     MM_K_LAYOUTS(128, 128, 2, 2),
     MM_K_LAYOUTS(64, 64, 2, 2),
+    MM_KSM(true, false),
+    MM_KSM(true, true),
+    MM_KSM(false, false),
+    MM_KSM(false, true),
     MM_K(256, 256, 2, 2, true, true, true),
     MM_K(128, 256, 2, 2, true, true, true),
     MM_K(128, 128, 2, 2, true, true, true),
@@ -608,6 +617,12 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     c.wgm = c.wgn = 2;
     c.pipe = 3;
   }
+  // 64 x 64 tiles of a short K take the kernel that holds all of K in LDS
+  // (one global round trip per tile instead of one per 64-k step); the
+  // basic kernel's own family (PIPE=0) keeps the basic kernel
+  if (!sk && !r.ffn && c.bm == 64 && c.bn == 64 && c.wgm == 2 && c.wgn == 2 && c.pipe != 0 &&
+      r.K <= mmk::kSmallKMax)
+    k = find_kernel(64, 64, 2, 2, a_kc, b_kc, false, 6);
   // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k && !sk; --fam) {
@@ -959,7 +974,8 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
               false, form == 1};
     Plan pl;
     if (plan_host(r, c, &pl) == MM_OK)
-      kernel = pl.kernel->pipe == 5   ? "gemm_pp"
+      kernel = pl.kernel->pipe == 6   ? "gemm_small"
+               : pl.kernel->pipe == 5 ? "gemm_pp"
                : pl.kernel->pipe == 4 ? "gemm_ws"
                : pl.kernel->pipe == 3 ? "gemm_nt_slab"
                : pl.kernel->pipe == 2 ? "gemm_pingpong"

@@ -139,7 +139,14 @@ def test_heuristic_choices():
     assert binding.describe_config("matmul", 8192, 8192, 8192, "tt").endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("ffn", 8192, 14336, 4096).startswith("BM=256,BN=256")
     small = binding.describe_config("matmul", 256, 256, 256, "nn")
-    assert small.startswith("BM=64,BN=64")
+    assert small.startswith("BM=64,BN=64") and small.endswith("KERNEL=gemm_small")
+    # all of K in LDS only up to K = 256; the basic kernel past it or under PIPE=0
+    assert binding.describe_config("matmul", 256, 256, 264, "nn").endswith("KERNEL=gemm_persistent")
+    binding.set_config("BM=64,BN=64,WM=2,WN=2,PIPE=0")
+    try:
+        assert binding.describe_config("matmul", 256, 256, 256, "nn").endswith("KERNEL=gemm_persistent")
+    finally:
+        binding.set_config(None)
     # long K turns on K-direction alternation
     assert "KALT=1" in binding.describe_config("matmul", 2047, 3001, 65536)
     assert "KALT=0" in binding.describe_config("matmul", 256, 256, 256)

@@ -43,6 +43,11 @@ CONFIGS = [
     "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=5",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
+    # 64 x 64 tiles: K <= 256 runs the kernel holding all of K in LDS (here
+    # on a small grid, several tiles per workgroup); PIPE=0 keeps the basic
+    # two-stage kernel at every K
+    "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0,GRID=3",
+    "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0,PIPE=0",
     # the slab instance that brings each tile's bias into LDS under the K
     # loop (bias epilogues of K-contiguous shapes with whole super-steps),
     # on a small grid so that the staging runs across several tiles
