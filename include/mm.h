@@ -225,7 +225,8 @@ mm_status mm_ffn_glu(const void* x, const void* W_gate, const void* W_up, void* 
  * preferred kernel family, 5 two-group ping-pong over alternate tiles and
  * 4 wave-specialized producer/consumer (both with BM=256,BN=128,WM=2,WN=4),
  * 3 whole-line slab ring, 2 split-phase on one tile, 1 32-k pipeline,
- * 0 basic; SK: stream-K chunks per tile when a workspace is given,
+ * 0 basic (64 x 64 tiles of K <= 256 otherwise take the kernel that holds
+ * all of K in LDS); SK: stream-K chunks per tile when a workspace is given,
  * 0 automatic, 1 never, n >= 2 forced; BSTAGE=1: linear forms with a bias
  * take the slab instance that brings the bias into LDS under the K loop).  The
  * heuristic is replaced for every later call in the process, in the manner
