@@ -250,3 +250,16 @@ def test_forced_band_height_is_clamped():
     assert big == two
     assert len(big) == 2 * 4096
     assert {(tm, tn) for (_, _, tm, tn, _) in big} == {(i, j) for i in range(2) for j in range(4096)}
+
+
+def test_c_program_uses_the_abi_without_a_gpu():
+    """tests/c/mm_from_c.c: the header and library used from plain C11
+    (argument errors, status strings, the configuration string)."""
+    import subprocess
+    import sys
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), "c"))
+    import build_c_test
+    exe = build_c_test.BIN if os.path.exists(build_c_test.BIN) else build_c_test.build()
+    r = subprocess.run([exe, "check"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().endswith("ok")
