@@ -293,10 +293,9 @@ def main() -> int:
     tiles = binding.describe_config(w.form, w.M, w.N, w.K, w.layout)
     cfg = dict(kv.split("=") for kv in tiles.split(","))
     ffn = str(w.form == "ffn").lower()
-    # the workspace the step passes ("auto") turns under-filled plain products
-    # into split-K: the slab kernel's split-K instance, then splitk_reduce
-    splitk = (w.form != "ffn" and w.epilogue == "none"
-              and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0)
+    # the workspace the step passes ("auto") turns under-filled products into
+    # split-K: the slab kernel's split-K instance, then splitk_reduce
+    splitk = w.form != "ffn" and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0
     bkn = str(w.layout in ("nn", "tn")).lower()
     amk = str(w.layout in ("tn", "tt")).lower()
     if splitk:

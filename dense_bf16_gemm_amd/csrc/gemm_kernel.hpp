@@ -112,6 +112,8 @@ struct SkReduceParams {
   int items;   // q, 0 = chunk-major
   int out_f32, out_vec;
   int tile_n;  // output columns per tile (256, or 192); slots stay 256 columns wide
+  const uint16_t* bias;  // [N], read when epi adds a bias
+  int epi;               // EPI_NONE / EPI_BIAS / EPI_GELU / EPI_BIAS_GELU, on the summed value
 };
 
 // A product with K = 0 (empty_k_fill): every sum over k is empty.

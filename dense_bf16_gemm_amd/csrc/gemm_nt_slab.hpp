@@ -869,8 +869,9 @@ gemm_nt_slab(GemmParams p) {
   }
 }
 
-// Second launch of a split-K product: out = the sum of the pieces' partial
-// tiles, in k order, rounded once to the output type.  Block b covers rows
+// Second launch of a split-K product: out = the epilogue of the sum of the
+// pieces' partial tiles (added in k order): + bias[n] and/or GELU, rounded
+// once to the output type.  Block b covers rows
 // 8 (b % 32) .. + 8 of tile b / 32.  Chunk-major: the pieces of tile t are the
 // slots j T + t, j = 0 .. n - 1.  Stream-K: chunk range [w q, (w + 1) q) of
 // workgroup w covers the tail of one tile and/or the head of the next; its
@@ -892,6 +893,8 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
     sstep = 1;
   }
   auto slot_of = [&](int w) { return p.items == 0 ? w : 2 * w + (t - (w * p.items) / p.chunks); };
+  const bool add_bias = p.epi == EPI_BIAS || p.epi == EPI_BIAS_GELU;
+  const bool gelu = p.epi == EPI_GELU || p.epi == EPI_BIAS_GELU;
   if (!p.out_vec) {
     // rows not 16-byte aligned: thread = one column of the 8 rows, so that
     // each load and each store of a wave covers consecutive elements
@@ -906,6 +909,12 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
         const float x = src[j * 256];
         v[j] = w == s0 ? x : v[j] + x;
       }
+    }
+    const float bn = add_bias ? __builtin_bit_cast(float, (uint32_t)p.bias[n] << 16) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] += bn;
+      if (gelu) v[j] = gelu_tanh(v[j]);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -937,6 +946,11 @@ __global__ void __launch_bounds__(256) splitk_reduce(SkReduceParams p) {
     }
   }
   const bool vec = n + 8 <= p.N;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (add_bias && n + j < p.N) v[j] += __builtin_bit_cast(float, (uint32_t)p.bias[n + j] << 16);
+    if (gelu) v[j] = gelu_tanh(v[j]);
+  }
   if (p.out_f32) {
     float* o = reinterpret_cast<float*>(p.out) + (int64_t)m * p.N + n;
     if (vec) {

@@ -500,12 +500,12 @@ constexpr int64_t kSkMaxWgs = 1024;  // bounds the workspace (at most 512 MiB)
 bool a_kcontig(int layout) { return layout == MM_NN || layout == MM_NT; }
 bool b_kcontig(int layout) { return layout == MM_NT || layout == MM_TT; }
 
-// plain products (no bias or activation: the pieces' sums meet before any
-// epilogue math would apply) in the slab kernel's domain: whole super-steps,
-// and 32-bit offsets within a tile's K-contiguous rows and a super-step's
-// k-rows of an operand stored [K][M] / [K][N]
+// single-output products of one weight (plain or linear; the reduction
+// applies the bias and GELU to the summed value) in the slab kernel's domain:
+// whole super-steps, and 32-bit offsets within a tile's K-contiguous rows and
+// a super-step's k-rows of an operand stored [K][M] / [K][N]
 bool splitk_shape(const Request& r) {
-  return r.batch == 1 && !r.ffn && r.epi == mmk::EPI_NONE && r.K % mmk::kSlabK == 0 &&
+  return r.batch == 1 && !r.ffn && !r.out_pre && r.K % mmk::kSlabK == 0 &&
          r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31) &&
          (a_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.M * 2 < (int64_t(1) << 31)) &&
          (b_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.N * 2 < (int64_t(1) << 31));
@@ -783,6 +783,8 @@ mm_status run(const Request& r, void* stream) {
     rp.out_f32 = pl.p.out_f32;
     rp.out_vec = pl.p.out_vec;
     rp.tile_n = sp.bn;
+    rp.bias = static_cast<const uint16_t*>(r.bias);
+    rp.epi = r.epi;
     void* rargs[] = {&rp};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::splitk_reduce), dim3((unsigned)(32 * rp.num_tiles)),
                         dim3(256), rargs, 0, static_cast<hipStream_t>(stream));

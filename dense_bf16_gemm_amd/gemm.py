@@ -125,7 +125,8 @@ def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None
            workspace="auto") -> torch.Tensor:
     """LinearOp form: out = epi(x @ W.T + bias) with x [M,K], W [N,K], bias [N],
     epilogue one of none | bias | gelu_tanh | bias_gelu_tanh; bf16 output.
-    `workspace` as for matmul (split-K applies to epilogue "none" only)."""
+    `workspace` as for matmul (a split product's reduction applies the
+    epilogue to the summed value)."""
     _check(x, "x")
     _check(W, "W")
     M, K = x.shape
@@ -146,8 +147,7 @@ def linear(x: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None
     elif out.shape != (M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [M, N] tensor")
     lib = binding.load()
-    wp, wb = (_resolve_ws(workspace, "linear", M, N, K, layout, x.device) if epilogue == "none"
-              else (None, 0))
+    wp, wb = _resolve_ws(workspace, "linear", M, N, K, layout, x.device)
     st = lib.mm_linear_ws(x.data_ptr(), W.data_ptr(), bias.data_ptr() if bias is not None else None,
                           out.data_ptr(), M, N, K, binding.LAYOUTS[layout],
                           binding.EPILOGUES[epilogue], wp, wb, _stream())

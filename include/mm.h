@@ -178,7 +178,9 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
  * one that overlaps an operand or the output returns MM_ERR_INVALID_VALUE.
  * A split call enqueues two kernels (the pieces, then their sum); a tile's
  * partial sums are added in k order, so results are reproducible run to run
- * (they differ from the unsplit kernel's by fp32 rounding order only).     */
+ * (they differ from the unsplit kernel's by fp32 rounding order only).  For
+ * mm_linear_ws the second kernel applies the epilogue (bias, GELU) to the
+ * summed value, then rounds once.                                          */
 mm_status mm_matmul_ws(const void* A, const void* B, void* out, int64_t M, int64_t N, int64_t K,
                        mm_layout layout, mm_out_dtype out_dtype, void* workspace,
                        int64_t workspace_bytes, void* stream);

@@ -491,6 +491,40 @@ def test_splitk_auto_workspace_two_streams(dev):
         assert not any(k[0] == dev.index for k in gemm_mod._workspaces)
 
 
+@pytest.mark.parametrize("case", [(520, 395, 8192, None),
+                                  (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
+def test_splitk_linear_epilogues(dev, case):
+    """Split-K of the linear form: the reduction adds the pieces in k order,
+    then applies the bias and GELU once.  Integer operands and bias keep the
+    bias epilogue bit-exact; the GELU epilogues (random operands) stay within
+    the bf16 tolerance; chunk-major and stream-K dealings, ragged tiles."""
+    M, N, K, cfg = case
+    binding.set_config(cfg)
+    try:
+        nbytes = binding.workspace_size("linear", M, N, K)
+        say("split-K linear", (M, N, K), cfg, nbytes)
+        assert nbytes > 0, "this shape should take the split-K path"
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
+        ops = synth.mapping_operands(M, N, K, "nt", seed=M + 9 * N + K, with_bias=True)
+        x, W, bias = ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev)
+        out = mm.linear(x, W, bias, "bias", workspace=ws)
+        torch.cuda.synchronize()
+        _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "bias",
+                              bias=synth.bits(ops["bias"]))
+        np.testing.assert_array_equal(to_bits(out), bits)
+        x = synth.randn_bf16((M, K), 1.0, 41)
+        W = synth.randn_bf16((N, K), K ** -0.5, 42)
+        b = synth.randn_bf16((N,), 1.0, 43)
+        for epi in ("gelu_tanh", "bias_gelu_tanh"):
+            out = mm.linear(x.to(dev), W.to(dev), b.to(dev) if "bias" in epi else None, epi, workspace=ws)
+            torch.cuda.synchronize()
+            y, _ = oracle.gemm(synth.bits(x), synth.bits(W), "nt", epi,
+                               bias=synth.bits(b) if "bias" in epi else None)
+            assert tol_excess(out.float().cpu().numpy(), y, 2e-2) <= 0, epi
+    finally:
+        binding.set_config(None)
+
+
 def test_splitk_random_and_fallbacks(dev):
     M, N, K = 700, 900, 16384
     x = synth.randn_bf16((M, K), 1.0, 11).to(dev)
