@@ -8,7 +8,8 @@ program's own (the outputs are overwritten, other kernels run, the host
 synchronizes), and every replay is checked, not just the first.  The cases
 cover the slab kernel with a fused epilogue, the horizontally fused FFN, and
 split-K with its two launches, through a caller's workspace and through the
-library's static scratch.
+library's static scratch, and a split linear form whose reduction applies
+the epilogue.
 """
 
 import pytest
@@ -61,13 +62,17 @@ def test_graph_replays_equal_eager_calls(dev):
     ws = torch.empty(binding.workspace_size("matmul", Ms, Ns, Ks, "nt"), dtype=torch.uint8, device=dev)
     y3 = torch.empty((Ms, Ns), dtype=torch.float32, device=dev)
     y4 = torch.empty((Ms, Ns), dtype=torch.float32, device=dev)
-    outs = (y1, y2, y3, y4)
+    # the same split with the linear form's epilogue, applied by the reduction
+    bias_s = synth.randn_bf16((Ns,), 1.0, 809).to(dev)
+    y5 = torch.empty((Ms, Ns), dtype=torch.bfloat16, device=dev)
+    outs = (y1, y2, y3, y4, y5)
 
     def calls():
         mm.linear(x, W, bias, "bias_gelu_tanh", out=y1)
         mm.ffn_swiglu(xf, Wg, Wu, out=y2)
         mm.matmul(As, Bs.t(), torch.float32, out=y3, workspace=ws)
         noalloc(As, Bs, Ms, Ns, Ks, y4)
+        mm.linear(As, Bs, bias_s, "bias_gelu_tanh", out=y5, workspace=ws)
 
     calls()
     torch.cuda.synchronize()
