@@ -300,16 +300,18 @@ def main() -> int:
     amk = str(w.layout in ("tn", "tt")).lower()
     if splitk:
         # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights,
-        # [K][M] activations, bias staged in LDS>; SPLIT=<chunks>x<tile width>
+        # [K][M] activations, bias staged in LDS, ragged K>;
+        # SPLIT=<chunks>x<tile width>
         chunks, bn = cfg.get("SPLIT", "0x256").split("x")
-        kernel = (f"mmk::gemm_nt_slab<256, {bn}, 2, 2, false, true, false, {bkn}, {amk}, false> + "
+        kernel = (f"mmk::gemm_nt_slab<256, {bn}, 2, 2, false, true, false, {bkn}, {amk}, false, false> + "
                   "mmk::splitk_reduce")
         tiles = f"BM=256,BN={bn},WM=2,WN=2,SPLITK={chunks},KERNEL=gemm_nt_slab+splitk_reduce"
     elif cfg["KERNEL"] == "gemm_nt_slab":
         bstage = str(cfg.get("BSTAGE") == "1" and w.form == "linear" and "bias" in w.epilogue
                      and w.layout == "nt").lower()
+        ragged = str(w.K % 64 != 0).lower()
         kernel = (f"mmk::gemm_nt_slab<{cfg['BM']}, {cfg['BN']}, {cfg['WM']}, {cfg['WN']}, {ffn}, "
-                  f"false, false, {bkn}, {amk}, {bstage}>")
+                  f"false, false, {bkn}, {amk}, {bstage}, {ragged}>")
     elif cfg["KERNEL"] == "gemm_small":
         kernel = (f"mmk::gemm_small<{str(w.layout in ('nn', 'nt')).lower()}, "
                   f"{str(w.layout in ('nt', 'tt')).lower()}>")

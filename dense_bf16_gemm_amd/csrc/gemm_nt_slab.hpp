@@ -171,7 +171,7 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 template <int BM, int BN, int WGM, int WGN, bool FFN, bool SPLITK = false, bool PRE = false,
-          bool BKN = false, bool AMK = false, bool BSTAGE = false>
+          bool BKN = false, bool AMK = false, bool BSTAGE = false, bool RAGGED = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_slab(GemmParams p) {
   // BKN: the weight operand is stored [K][N] (the MatmulOp form's B as
@@ -187,6 +187,12 @@ gemm_nt_slab(GemmParams p) {
   // (see copy_bias); built for the K-contiguous linear form with bias.
   static_assert(!(BSTAGE && (FFN || SPLITK || PRE || BKN || AMK)), "bias staging: plain linear form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
+  // RAGGED: K is not a multiple of 64 (it is one of 8: K-contiguous rows).
+  // The tile's last super-step is a partial one: its copies push the lanes
+  // whose 16-byte chunk lies past K out of the buffer range, so those chunks
+  // arrive as zeros (see tail_bits).
+  static_assert(!(RAGGED && (FFN || SPLITK || PRE || BKN || AMK || BSTAGE)),
+                "ragged K: K-contiguous single-weight single-output forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
   // changes the register allocation of its K loop.
@@ -198,9 +204,10 @@ gemm_nt_slab(GemmParams p) {
   constexpr int FN = WTN / 16;
   constexpr int OUT_BN = FFN ? BN / 2 : BN;
   constexpr int UNIT = 256 * kSlabRowB;  // 32 KiB
-  // BN = 192 (a 128 x 96 block per wave): the split-K instance for products
-  // whose 256 x 256 tiles would leave a quarter of the grid idle
-  static_assert(BM == 256 && (BN == 256 || (BN == 192 && SPLITK && !BKN && !AMK)) && NW == 4,
+  // BN = 192 (a 128 x 96 block per wave): K-contiguous single-weight products
+  // whose 256 x 256 tiles would leave much of the grid idle (split or not)
+  static_assert(BM == 256 && (BN == 256 || (BN == 192 && !BKN && !AMK && !FFN && !PRE && !BSTAGE)) &&
+                    NW == 4,
                 "a unit holds 256 rows; four waves");
   static_assert(FM == 8 && (FN == 8 || FN == 6), "row schedule assumes 8 x 8 (or 8 x 6) fragments per wave");
   constexpr int CPS = BM / 8 / NW;     // 1 KiB activation copies per wave per slab
@@ -219,7 +226,7 @@ gemm_nt_slab(GemmParams p) {
   // wave-uniform results back to scalar registers, so that all descriptor
   // and offset arithmetic below stays scalar)
   const int wg = __builtin_amdgcn_readfirstlane(remap_workgroup(blockIdx.x, G, p.xcd_remap));
-  const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2)
+  const int KS = p.k_tiles;  // super-steps of 64 per tile (>= 2; the last partial when RAGGED)
   // work units: tiles (of every batch entry), or (stream-K) the one or two
   // pieces of this workgroup's chunk range [ci0, ci1)
   // (sk_items == 0: chunk-major split-K, workgroup c runs chunk c / tiles of
@@ -243,6 +250,13 @@ gemm_nt_slab(GemmParams p) {
   const int cchunk = (lane & 7) ^ lds_swz(crow + 8 * (wave & 2));
   const uint32_t row_bytes = (uint32_t)ld * 2u;
   const uint32_t lane_base = (uint32_t)crow * row_bytes + 16u * (uint32_t)cchunk;
+  // RAGGED: the copies of a tile's partial last super-step OR tail_bits into
+  // their lane offsets; it is lane_oob there (bit 31 for a lane whose chunk,
+  // 8 cchunk values of k past the super-step's first, lies past K: the offset
+  // then exceeds the record, below 2^31, and the chunk reads as zeros) and 0
+  // in every other super-step
+  const uint32_t lane_oob = RAGGED && 8 * cchunk >= (K & 63) ? 0x80000000u : 0u;
+  uint32_t tail_bits = 0u;
   constexpr int kRsrcWord3 = 0x00020000;
   // [K][N] weight slab: copy c of this wave fills unit rows 2j, 2j + 1 (k),
   // j = 4c + wave, 512 bytes each; lane L fills row 2j + L/32, physical
@@ -389,7 +403,7 @@ gemm_nt_slab(GemmParams p) {
     const __amdgpu_buffer_rsrc_t r = rsrc(cur.a_base + kbytes, cur.a_rec - kbytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
-        lane_base + (uint32_t)(8 * (c * NW + wave)) * row_bytes, 0, 0, 0);
+        (lane_base + (uint32_t)(8 * (c * NW + wave)) * row_bytes) | tail_bits, 0, 0, 0);
   };
   auto copy_b = [&](int c, uint32_t kbytes, int unit) __attribute__((always_inline)) {
     if constexpr (BKN) {
@@ -408,7 +422,7 @@ gemm_nt_slab(GemmParams p) {
     const __amdgpu_buffer_rsrc_t r = rsrc((up ? cur.b1_base : cur.b0_base) + kbytes, cur.b_rec - kbytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(smem + unit * UNIT + (c * NW + wave) * 1024), 16,
-        lane_base + (uint32_t)prow * row_bytes, 0, 0, 0);
+        (lane_base + (uint32_t)prow * row_bytes) | tail_bits, 0, 0, 0);
   };
   auto next_unit = [](int u) __attribute__((always_inline)) {
     return u + 1 == kSlabUnits ? 0 : u + 1;
@@ -495,7 +509,9 @@ gemm_nt_slab(GemmParams p) {
     // prologue: slabs of super-steps 0 and 1 of the first tile (KS >= 2)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t kbytes = 2u * (uint32_t)k0_of(s);
+      const int k0 = k0_of(s);
+      const uint32_t kbytes = 2u * (uint32_t)k0;
+      if constexpr (RAGGED) tail_bits = k0 + kSlabK > K ? lane_oob : 0u;  // a reversed tile starts with it
 #pragma unroll
       for (int c = 0; c < CPS; ++c) copy_a(c, kbytes, 2 * s);
 #pragma unroll
@@ -554,6 +570,7 @@ gemm_nt_slab(GemmParams p) {
   };
   auto super_step = [&](int k0_fetch) __attribute__((always_inline)) {
     const uint32_t kbytes = 2u * (uint32_t)k0_fetch;
+    if constexpr (RAGGED) tail_bits = k0_fetch + kSlabK > K ? lane_oob : 0u;
     const int ua = cur_unit, ub = next_unit(ua);
     const int nua = next_unit(ub), nub = next_unit(nua);  // super-step q+1
     const int cua = next_unit(nub);                        // A slab of q+2

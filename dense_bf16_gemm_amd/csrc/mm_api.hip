@@ -63,6 +63,7 @@ struct KernelEntry {
   bool splitk = false;         // gemm_nt_slab<..., SPLITK>: needs a workspace
   bool pre = false;            // gemm_nt_slab<..., PRE>: stores the pre-activation too
   bool bstage = false;         // gemm_nt_slab<..., BSTAGE>: stages the bias through LDS
+  bool ragged = false;         // gemm_nt_slab<..., RAGGED>: K not a multiple of 64
 };
 
 #define MM_K(BM, BN, WGM, WGN, AKC, BKC, FFN)                                              \
@@ -107,6 +108,18 @@ struct KernelEntry {
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC)>), {0}}
 
 // the plain linear form with the bias brought into LDS under the K loop
+// the single-weight linear / plain form on 256 x 192 tiles (K-contiguous)
+#define MM_KS192()                                                                         \
+  {256, 192, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 192, 2, 2, false>), {0}}
+
+// K not a multiple of 64 (K-contiguous single-weight products)
+#define MM_KSR(BN)                                                                         \
+  {256, BN, 2, 2, true, true, false, 3,                                                    \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, BN, 2, 2, false, false, false, false, false, false, true>), \
+   {0}, false, false, false, true}
+
 #define MM_KSB()                                                                           \
   {256, 256, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(                                                          \
@@ -141,6 +154,9 @@ KernelEntry g_kernels[] = {
     MM_KPPT(),
     MM_KS(false),
     MM_KS(true),
+    MM_KS192(),
+    MM_KSR(256),
+    MM_KSR(192),
     MM_KPP(false),
     MM_KPP(true),
     MM_KP(256, 256, 2, 4, false),
@@ -165,11 +181,11 @@ KernelEntry g_kernels[] = {
 };
 
 KernelEntry* find_kernel(int bm, int bn, int wgm, int wgn, bool a_kc, bool b_kc, bool ffn, int pipe,
-                         bool splitk = false, bool pre = false, bool bstage = false) {
+                         bool splitk = false, bool pre = false, bool bstage = false, bool ragged = false) {
   for (auto& k : g_kernels)
     if (k.bm == bm && k.bn == bn && k.wgm == wgm && k.wgn == wgn && k.a_kc == a_kc &&
         k.b_kc == b_kc && k.ffn == ffn && k.pipe == pipe && k.splitk == splitk && k.pre == pre &&
-        k.bstage == bstage)
+        k.bstage == bstage && k.ragged == ragged)
       return &k;
   return nullptr;
 }
@@ -271,7 +287,11 @@ Config heuristic(bool ffn, int64_t M, int64_t N, int64_t K) {
       c.bm = 128; c.bn = 128;
     }
   } else {
-    if (cdiv(M, 256) * cdiv(N, 256) >= 192) {
+    // 256 x 256 tiles once they occupy half of the CUs: at 3072^3 (144 tiles)
+    // linear + bias + GELU took 56.2 us on them against 112.5 us on 128 x 128
+    // tiles (the 32-k pipeline); at 2560^3 (100 tiles) 48.5 against 49.4; at
+    // 2048^3 (64 tiles) 40.7 against 25.9
+    if (cdiv(M, 256) * cdiv(N, 256) >= 128) {
       c.bm = 256; c.bn = 256;
     } else if (cdiv(M, 128) * cdiv(N, 128) >= 64) {
       c.bm = 128; c.bn = 128;
@@ -543,11 +563,13 @@ SkPlan splitk_plan_bn(const Request& r, const Config& c, int64_t wgs, int bn) {
     // 4: 941, 5: 849, 8: 948, 16: 1287; unsplit 1165)
     n = (int)cdiv(3 * wgs, 4 * T);
     if (n > 16) n = 16;
-    while (n > 2 && (KS / n < 8 || n * T > wgs)) --n;
-    // a piece runs at least eight super-steps: shorter K loops do not pay for
-    // the partial tiles and the second launch (256^3 in two pieces: 14.0 us
-    // of pieces plus 3.8 us of reduction)
-    if (KS / n < 8) return sp;
+    while (n > 2 && (KS / n < 32 || n * T > wgs)) --n;
+    // a piece runs at least 32 super-steps (K >= 2048): shorter K loops do not
+    // pay for the partial tiles and the second launch (linear + bias + GELU
+    // at 2048^3: 39.5 us split in three against 25.9 unsplit; 1000 x 3001 x
+    // 2048 in four: 34.1 against 28.2; 256^3 in two: 16.5 against 10.9),
+    // longer ones do (1024 x 8192 x 8192 in two: 117.5 against 151.8)
+    if (KS / n < 32) return sp;
   } else {
     return sp;
   }
@@ -623,6 +645,15 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   if (!sk && !r.ffn && c.bm == 64 && c.bn == 64 && c.wgm == 2 && c.wgn == 2 && c.pipe != 0 &&
       r.K <= mmk::kSmallKMax)
     k = find_kernel(64, 64, 2, 2, a_kc, b_kc, false, 6);
+  // 256 x 192 tiles exist for the slab kernel's K-contiguous single-weight
+  // single-output form only; other requests under such a configuration run
+  // 256 x 256 tiles
+  if (!sk && c.bn == 192 &&
+      !(a_kc && b_kc && !r.ffn && !r.out_pre && r.K >= 2 * mmk::kSlabK &&
+        (int64_t)256 * r.K * 2 < (int64_t(1) << 31))) {
+    c.bm = c.bn = 256;
+    c.wgm = c.wgn = 2;
+  }
   // the pipelined kernels address a tile's rows with 32-bit buffer offsets
   const int64_t span = (int64_t)(c.bm > c.bn ? c.bm : c.bn) * r.K * 2;
   for (int fam = c.pipe; fam >= 0 && !k && !sk; --fam) {
@@ -633,8 +664,12 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // the ping-pong and wave-specialized kernels only under their own
     // configuration (fam == c.pipe), never as another family's fallback
     if ((fam == 4 || fam == 5) && fam != c.pipe) continue;
-    // the slab kernel runs whole super-steps of 64 k, two of them in flight
-    if (fam == 3 && (r.K % mmk::kSlabK != 0 || r.K < 2 * mmk::kSlabK)) continue;
+    // the slab kernel runs whole super-steps of 64 k, two of them in flight;
+    // a K that is not a multiple of 64 takes its RAGGED instance (K-contiguous
+    // single-weight single-output products: the tail after the loop)
+    const bool ragged = fam == 3 && r.K % mmk::kSlabK != 0;
+    if (fam == 3 && r.K < 2 * mmk::kSlabK) continue;
+    if (ragged && !(a_kc && b_kc && !r.ffn && !r.out_pre)) continue;
     // its [K][N]-weight and [K][M]-activation forms address a super-step's
     // 64 k-rows of such an operand with 32-bit buffer offsets
     if (fam == 3 && !b_kc && (int64_t)mmk::kSlabK * r.N * 2 >= (int64_t(1) << 31)) continue;
@@ -642,8 +677,9 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // the bias-staging instance: K-contiguous single-weight linear forms
     // with a bias epilogue, when the configuration asks for it
     const bool bstage = fam == 3 && c.bstage && a_kc && b_kc && !r.ffn && !r.out_pre && r.batch == 1 &&
-                        (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
-    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre, bstage);
+                        !ragged && (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
+    k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre, bstage,
+                    ragged);
   }
   // layouts a wave grid is not built for run the 2 x 2 kernel of the same tile
   if (!k) k = find_kernel(c.bm, c.bn, 2, 2, a_kc, b_kc, r.ffn, 0);
@@ -700,6 +736,28 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   return MM_OK;
 }
 
+// The heuristic's configuration for a request: its 256 x 256 tiles become
+// 256 x 192 for a K-contiguous single-weight product when that takes fewer
+// passes of a 256-CU grid, weighed by the narrower tile's cost (a 256 x 192
+// super-step of operands served by the Infinity Cache took ~1760 cycles
+// against ~2246 for 256 x 256: 0.78 of the time for 0.75 of the work).
+// 6144^3 (576 tiles, 2.25 passes) and 3072^3 (144 tiles, half the CUs idle)
+// take it; 8192^3 (4 passes against 6) does not.  A forced configuration is
+// kept as it is.
+Config choose_config_for(const Request& r) {
+  Config c = choose_config(r.ffn, r.M, r.N, r.K);
+  if (c.forced || c.bm != 256 || c.bn != 256 || c.wgm != 2 || c.wgn != 2 || c.pipe != 3 || c.bstage)
+    return c;
+  if (r.ffn || r.out_pre || r.batch != 1 || !a_kcontig(r.layout) || !b_kcontig(r.layout) ||
+      r.K < 2 * mmk::kSlabK || (int64_t)256 * r.K * 2 >= (int64_t(1) << 31))
+    return c;
+  constexpr int64_t kGrid = 256;
+  const int64_t passes256 = cdiv(cdiv(r.M, 256) * cdiv(r.N, 256), kGrid);
+  const int64_t passes192 = cdiv(cdiv(r.M, 256) * cdiv(r.N, 192), kGrid);
+  if (passes192 * 78 < passes256 * 100) c.bn = 192;
+  return c;
+}
+
 // K == 0: one launch of empty_k_fill over every output element
 mm_status run_empty_k(const Request& r, void* stream) {
   mmk::EmptyKParams p;
@@ -725,7 +783,7 @@ mm_status run(const Request& r, void* stream) {
   if (s != MM_OK) return s;
   if (r.M == 0 || r.N == 0) return MM_OK;
   if (r.K == 0) return run_empty_k(r, stream);
-  const Config c = choose_config(r.ffn, r.M, r.N, r.K);
+  const Config c = choose_config_for(r);
   Plan pl;
   SkPlan sp;
   s = plan_host(r, c, &pl);
@@ -881,7 +939,7 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
   Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
             false, form == 1};
   if (M == 0 || N == 0 || K == 0 || !splitk_shape(r)) return MM_OK;
-  const Config c = choose_config(r.ffn, M, N, K);
+  const Config c = choose_config_for(r);
   if (c.sk == 1) return MM_OK;
   int cus = 0, occ = 0;
   mm_status s;
@@ -968,12 +1026,13 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
   if (!buf || buflen <= 0 || (form != 0 && form != 1) || M < 0 || N < 0 || K < 0 ||
       layout < MM_NN || layout > MM_TT)
     return fail(MM_ERR_INVALID_VALUE, "bad arguments");
-  const Config c = choose_config(form == 1, M, N, K);
+  const Request rq{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
+                   false, form == 1};
+  const Config c = choose_config_for(rq);
   // the kernel a call of this shape would launch (no HIP call is made)
   const char* kernel = M > 0 && N > 0 && K == 0 ? "empty_k_fill" : "none";
   if (M > 0 && N > 0 && K > 0) {
-    Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
-              false, form == 1};
+    const Request& r = rq;
     Plan pl;
     if (plan_host(r, c, &pl) == MM_OK)
       kernel = pl.kernel->pipe == 6   ? "gemm_small"
@@ -1015,7 +1074,7 @@ mm_status mm_debug_schedule(int form, int64_t M, int64_t N, int64_t K, mm_layout
     return fail(MM_ERR_INVALID_VALUE, "bad arguments");
   Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
             false, form == 1};
-  const Config c = choose_config(form == 1, M, N, K);
+  const Config c = choose_config_for(r);
   Plan pl;
   mm_status s = plan_host(r, c, &pl);
   if (s != MM_OK) return s;

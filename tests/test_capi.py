@@ -126,13 +126,18 @@ def test_config_override_and_rejection(lib):
 def test_heuristic_choices():
     assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=256,BN=256")
     # K-contiguous 256 x 256 tiles run the whole-line slab kernel when K spans two
-    # super-steps of 64, the 32-k pipeline otherwise; [K][N] weights and [K][M]
-    # activations (NN, TN, TT) run the slab kernel's transpose-read forms for
-    # whole super-steps, the basic kernel for other K
+    # super-steps of 64 (a partial last one through the ragged instance for a
+    # single weight, the 32-k pipeline for the FFN), the 32-k pipeline below
+    # that; [K][N] weights and [K][M] activations (NN, TN, TT) run the slab
+    # kernel's transpose-read forms for whole super-steps, the basic kernel
+    # for other K
     assert binding.describe_config("linear", 8192, 8192, 8192).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("ffn", 8192, 14336, 4096).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("linear", 8192, 8192, 64).endswith("KERNEL=gemm_nt_pipe")
-    assert binding.describe_config("linear", 8192, 8192, 8200).endswith("KERNEL=gemm_nt_pipe")
+    assert binding.describe_config("linear", 8192, 8192, 8200).endswith("KERNEL=gemm_nt_slab")
+    assert binding.describe_config("linear", 8192, 8192, 136).endswith("KERNEL=gemm_nt_slab")
+    assert binding.describe_config("linear", 8192, 8192, 120).endswith("KERNEL=gemm_nt_pipe")
+    assert binding.describe_config("ffn", 8192, 14336, 4104).endswith("KERNEL=gemm_nt_pipe")
     assert binding.describe_config("matmul", 8192, 8192, 8192, "nn").endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("matmul", 8192, 8192, 8200, "nn").endswith("KERNEL=gemm_persistent")
     assert binding.describe_config("matmul", 8192, 8192, 8192, "tn").endswith("KERNEL=gemm_nt_slab")

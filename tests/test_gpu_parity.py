@@ -43,6 +43,10 @@ CONFIGS = [
     "BM=256,BN=128,WM=2,WN=4,G=2,XCD=0,KALT=2,GRID=3,PIPE=5",
     "BM=128,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1",
     "BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0",
+    # 256 x 192 tiles (K-contiguous single-weight products; other layouts
+    # and forms fall back to 256 x 256), also on a small grid
+    "BM=256,BN=192,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3",
+    "BM=256,BN=192,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     # 64 x 64 tiles: K <= 256 runs the kernel holding all of K in LDS (here
     # on a small grid, several tiles per workgroup); PIPE=0 keeps the basic
     # two-stage kernel at every K
@@ -142,12 +146,14 @@ def shapes_for(layout):
 
 def test_ws_config_selects_ws_kernel():
     """PIPE=4 runs the wave-specialized kernel where it applies and the default
-    slab tile elsewhere (ragged K, FFN)."""
+    slab tile elsewhere (a partial last super-step, FFN), the 32-k pipeline
+    below two super-steps."""
     binding.set_config("BM=256,BN=128,WM=2,WN=4,G=8,XCD=1,KALT=2,PIPE=4")
     try:
         for (M, N, K) in shapes_for("nt")[-3:]:
             assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_ws")
-        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_pipe")
+        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_slab")
+        assert binding.describe_config("linear", 300, 267, 72).endswith("KERNEL=gemm_nt_pipe")
         assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
     finally:
         binding.set_config(None)
@@ -160,7 +166,8 @@ def test_pp_config_selects_pp_kernel():
     try:
         for (M, N, K) in shapes_for("nt")[-3:]:
             assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_pp")
-        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_pipe")
+        assert binding.describe_config("linear", 300, 267, 200).endswith("KERNEL=gemm_nt_slab")
+        assert binding.describe_config("linear", 300, 267, 72).endswith("KERNEL=gemm_nt_pipe")
         assert binding.describe_config("ffn", 300, 515, 256).endswith("KERNEL=gemm_nt_slab")
         assert binding.describe_config("matmul", 520, 392, 4160, "nn").endswith("KERNEL=gemm_nt_slab")
     finally:
@@ -762,6 +769,83 @@ def test_workload_mapping_bitexact(dev, name):
     else:
         bad = np.argwhere(to_bits(got) != ref_bits)
     assert bad.size == 0, f"{name}: {len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+# shapes the heuristic gives 256 x 192 tiles (fewer passes of the grid than
+# 256 x 256): one full pass, one with ragged last tile rows and columns, and
+# three passes
+NARROW_SHAPES = [(3072, 3072, 3072), (2900, 3000, 2048), (6144, 6144, 6144)]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES)
+def test_narrow_tiles_default_path(dev, shape):
+    """The default configuration's 256 x 192 tiles: the index mapping bit for
+    bit with integer operands (every output element, guard bands), and
+    linear + bias + GELU on random operands within the bf16 tolerance."""
+    M, N, K = shape
+    cfg = binding.describe_config("linear", M, N, K)
+    say("narrow tiles", shape, cfg)
+    assert cfg.startswith("BM=256,BN=192") and cfg.endswith("KERNEL=gemm_nt_slab"), cfg
+    ops = synth.mapping_operands(M, N, K, "nt", seed=M + N + K, with_bias=True)
+    buf, out = guarded_out(M, N, False, dev)
+    mm.linear(ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev), "bias", out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    got = to_bits(out)
+    _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "bias",
+                          bias=synth.bits(ops["bias"]))
+    bad = np.argwhere(got != bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    x = synth.randn_bf16((M, K), 1.0, 51)
+    W = synth.randn_bf16((N, K), K ** -0.5, 52)
+    b = synth.randn_bf16((N,), 1.0, 53)
+    got = mm.linear(x.to(dev), W.to(dev), b.to(dev), "bias_gelu_tanh")
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(W), "nt", "bias_gelu_tanh", bias=synth.bits(b))
+    assert tol_excess(got.float().cpu().numpy(), y, 2e-2) <= 0
+
+
+# K not a multiple of 64 on the default path: the slab kernel's last
+# super-step of every tile is a partial one (its copies fetch zeros past K).
+# 256 x 192 tiles with a 56-k and an 8-k tail (the first with K alternation,
+# so half the tiles start with the partial super-step), 256 x 256 tiles with
+# an 8-k tail, and a mid-size shape that the heuristic gives 128 x 128 tiles.
+RAGGED_SHAPES = [(3000, 3000, 3000), (2900, 3000, 1032), (4096, 4096, 4168), (1000, 1000, 3080)]
+
+
+@pytest.mark.parametrize("shape", RAGGED_SHAPES)
+def test_ragged_k_default_path(dev, shape):
+    """Every output element bit for bit with integer operands (guard bands
+    checked), then linear + bias + GELU on random operands within the bf16
+    tolerance, and an fp32 matmul of dense integers bit for bit."""
+    M, N, K = shape
+    cfg = binding.describe_config("linear", M, N, K)
+    say("ragged K", shape, cfg)
+    if M * N >= 2000 * 2000:
+        assert cfg.endswith("KERNEL=gemm_nt_slab"), cfg
+    ops = synth.mapping_operands(M, N, K, "nt", seed=M + N + K, with_bias=True)
+    buf, out = guarded_out(M, N, False, dev)
+    mm.linear(ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev), "bias", out=out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "bias",
+                          bias=synth.bits(ops["bias"]))
+    bad = np.argwhere(to_bits(out) != bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    del buf, out
+    x = synth.randn_bf16((M, K), 1.0, 61)
+    W = synth.randn_bf16((N, K), K ** -0.5, 62)
+    b = synth.randn_bf16((N,), 1.0, 63)
+    got = mm.linear(x.to(dev), W.to(dev), b.to(dev), "bias_gelu_tanh")
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(W), "nt", "bias_gelu_tanh", bias=synth.bits(b))
+    assert tol_excess(got.float().cpu().numpy(), y, 2e-2) <= 0
+    A, B = synth.dense_int_operands(M, N, K, "nt", seed=7)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    call_matmul(A.to(dev), B.to(dev), M, N, K, "nt", True, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm(synth.bits(A), synth.bits(B), "nt")
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
 # ------------------------------------------------------------ edge cases

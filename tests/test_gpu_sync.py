@@ -170,3 +170,43 @@ def test_linear_bias_staged(libs, grid):
         assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
             A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
             binding.LAYOUTS["nt"], binding.EPILOGUES[epi], stream()), "mm_linear"), [out]))
+
+
+@pytest.mark.parametrize("grid", [0, 5])
+def test_linear_narrow_tiles(libs, grid):
+    """The 256 x 192 instance of the slab kernel (ragged tiles; on a grid of
+    5 the ring runs on across several tiles per workgroup)."""
+    dev = torch.device("cuda:0")
+    M, N, K = 1040, 776, 1024
+    cfg = f"BM=256,BN=192,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
+    A, B = operands(M, N, K, "nt", 990 + grid, dev)
+    bias = synth.randn_bf16((N,), 1.0, 995).to(dev)
+    assert_slab(libs, cfg, "linear", M, N, K, "nt")
+    say("linear, 256 x 192 tiles", (M, N, K), cfg)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
+        A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
+        binding.LAYOUTS["nt"], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))
+    out32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_matmul(
+        A.data_ptr(), B.data_ptr(), out32.data_ptr(), M, N, K, binding.LAYOUTS["nt"], 1, stream()),
+        "mm_matmul"), [out32]))
+
+
+@pytest.mark.parametrize("bn", [256, 192])
+@pytest.mark.parametrize("grid", [0, 5])
+def test_ragged_k(libs, bn, grid):
+    """The instance whose last super-step per tile is a partial one (K = 1000:
+    15 whole super-steps and 40 k more; with K alternation half the tiles
+    fetch the partial one first)."""
+    dev = torch.device("cuda:0")
+    M, N, K = 1040, 776, 1000
+    cfg = f"BM=256,BN={bn},WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
+    A, B = operands(M, N, K, "nt", 1000 + grid, dev)
+    bias = synth.randn_bf16((N,), 1.0, 1005).to(dev)
+    assert_slab(libs, cfg, "linear", M, N, K, "nt")
+    say("linear, ragged K", (M, N, K), cfg)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
+        A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
+        binding.LAYOUTS["nt"], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))

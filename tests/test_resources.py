@@ -33,7 +33,7 @@ SPILL_BUDGET_256ACC = {"VGPRs Spill": 8, "SGPRs Spill": 8, "ScratchSize [bytes/l
 # staging state in scalar registers across its K loop; its scalar spills go
 # to vector-register lanes outside the loop (test_no_lane_spills_in_mfma_loops).
 SPILL_BUDGET_OVERRIDE = {
-    "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb1EEEvNS_10GemmParamsE":
+    "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb1ELb0EEEvNS_10GemmParamsE":
         {"SGPRs Spill": 12},
 }
 
@@ -312,7 +312,7 @@ def test_no_lane_spills_in_mfma_loops(disassembly):
 def test_headline_kernel_k_loop_shape(disassembly):
     """The 256 x 256 slab kernel's K loop: 128 MFMAs per 64-k super-step (a
     multiple of it if unrolled), one barrier per super-step, no scratch."""
-    name = "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb0EEEvNS_10GemmParamsE"
+    name = "_ZN3mmk12gemm_nt_slabILi256ELi256ELi2ELi2ELb0ELb0ELb0ELb0ELb0ELb0ELb0EEEvNS_10GemmParamsE"
     code = disassembly[name]
     loops = _k_loops(code)
     assert len(loops) == 1, len(loops)

@@ -47,9 +47,9 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 
 
 # (M, N, K, layout): two calls in a row, the second smaller, both split by the
-# automatic rule (20 tiles of 256 x 192 in 10 chunks: 200 slots = 50 MiB of
-# scratch; then 9 tiles in 16 chunks: 144 slots); then a stored-[K][N]
-# product (256 x 256 tiles) and a shape that runs unsplit
+# automatic rule (20 tiles of 256 x 192 in 8 chunks: 160 slots = 40 MiB of
+# scratch; then 9 tiles in 4 chunks: 36 slots); then a stored-[K][N] product
+# (256 x 256 tiles) and a shape that runs unsplit
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
             (520, 392, 512, "nt")]
 
