@@ -187,12 +187,15 @@ gemm_nt_slab(GemmParams p) {
   // (see copy_bias); built for the K-contiguous linear form with bias.
   static_assert(!(BSTAGE && (FFN || SPLITK || PRE || BKN || AMK)), "bias staging: plain linear form only");
   static_assert(!(SPLITK && FFN), "split-K is built for the single-weight forms");
-  // RAGGED: K is not a multiple of 64 (it is one of 8: K-contiguous rows).
-  // The tile's last super-step is a partial one: its copies push the lanes
-  // whose 16-byte chunk lies past K out of the buffer range, so those chunks
-  // arrive as zeros (see tail_bits).
-  static_assert(!(RAGGED && (FFN || SPLITK || PRE || BKN || AMK || BSTAGE)),
-                "ragged K: K-contiguous single-weight single-output forms");
+  // RAGGED: K is not a multiple of 64 (it is one of 8, the alignment of
+  // K-contiguous rows).  The tile's last super-step is a partial one.  A
+  // K-contiguous operand's copies push the lanes whose 16-byte chunk lies past
+  // K out of the buffer range, so those chunks arrive as zeros (see
+  // tail_bits); an operand stored [K][N] or [K][M] needs nothing: its k-rows
+  // past K lie past the end of the matrix, outside the record, and read as
+  // zeros too.
+  static_assert(!(RAGGED && (FFN || SPLITK || PRE || BSTAGE)),
+                "ragged K: single-weight single-output forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
   // changes the register allocation of its K loop.

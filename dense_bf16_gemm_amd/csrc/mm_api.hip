@@ -107,19 +107,25 @@ struct KernelEntry {
   {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC)>), {0}}
 
-// the plain linear form with the bias brought into LDS under the K loop
 // the single-weight linear / plain form on 256 x 192 tiles (K-contiguous)
 #define MM_KS192()                                                                         \
   {256, 192, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 192, 2, 2, false>), {0}}
 
-// K not a multiple of 64 (K-contiguous single-weight products)
+// K not a multiple of 64 (single-weight products; 256 x 192 tiles for
+// K-contiguous operands only)
 #define MM_KSR(BN)                                                                         \
   {256, BN, 2, 2, true, true, false, 3,                                                    \
    reinterpret_cast<const void*>(                                                          \
        &mmk::gemm_nt_slab<256, BN, 2, 2, false, false, false, false, false, false, true>), \
    {0}, false, false, false, true}
+#define MM_KSRKN(AKC, BKC)                                                                 \
+  {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC), false, true>), \
+   {0}, false, false, false, true}
 
+// the plain linear form with the bias brought into LDS under the K loop
 #define MM_KSB()                                                                           \
   {256, 256, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(                                                          \
@@ -157,6 +163,9 @@ KernelEntry g_kernels[] = {
     MM_KS192(),
     MM_KSR(256),
     MM_KSR(192),
+    MM_KSRKN(true, false),
+    MM_KSRKN(false, false),
+    MM_KSRKN(false, true),
     MM_KPP(false),
     MM_KPP(true),
     MM_KP(256, 256, 2, 4, false),
@@ -664,12 +673,12 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // the ping-pong and wave-specialized kernels only under their own
     // configuration (fam == c.pipe), never as another family's fallback
     if ((fam == 4 || fam == 5) && fam != c.pipe) continue;
-    // the slab kernel runs whole super-steps of 64 k, two of them in flight;
-    // a K that is not a multiple of 64 takes its RAGGED instance (K-contiguous
-    // single-weight single-output products: the tail after the loop)
+    // the slab kernel runs super-steps of 64 k, two of them in flight; a K
+    // that is not a multiple of 64 takes its RAGGED instance (single-weight
+    // single-output products: the last super-step reads zeros past K)
     const bool ragged = fam == 3 && r.K % mmk::kSlabK != 0;
     if (fam == 3 && r.K < 2 * mmk::kSlabK) continue;
-    if (ragged && !(a_kc && b_kc && !r.ffn && !r.out_pre)) continue;
+    if (ragged && (r.ffn || r.out_pre)) continue;
     // its [K][N]-weight and [K][M]-activation forms address a super-step's
     // 64 k-rows of such an operand with 32-bit buffer offsets
     if (fam == 3 && !b_kc && (int64_t)mmk::kSlabK * r.N * 2 >= (int64_t(1) << 31)) continue;

@@ -848,6 +848,60 @@ def test_ragged_k_default_path(dev, shape):
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_ragged_k_transposed_storage(dev, layout):
+    """K not a multiple of 64 with operands stored [K][N] and/or [K][M] on the
+    default path (the transpose-read slab forms; their k-rows past K lie past
+    the end of the matrix): bit for bit with integer operands, bf16 with a
+    bias and fp32, guard bands checked."""
+    M, N, K = 4000, 3000, 1032
+    cfg = binding.describe_config("linear", M, N, K, layout)
+    say("ragged K", layout, (M, N, K), cfg)
+    assert cfg.endswith("KERNEL=gemm_nt_slab"), cfg
+    ops = synth.mapping_operands(M, N, K, layout, seed=M + N + K + 1, with_bias=True)
+    buf, out = guarded_out(M, N, False, dev)
+    call_linear(ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev), M, N, K, layout, "bias", out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), layout, "bias",
+                          bias=synth.bits(ops["bias"]))
+    bad = np.argwhere(to_bits(out) != bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    del buf, out
+    A, B = synth.dense_int_operands(M, N, K, layout, seed=9)
+    buf, out = guarded_out(M, N, True, dev)
+    call_matmul(A.to(dev), B.to(dev), M, N, K, layout, True, out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    ref, _ = oracle.gemm(synth.bits(A), synth.bits(B), layout)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+def test_batched_ragged_k_slab(dev, layout):
+    """Batched products with K not a multiple of 64 on the slab kernel (a
+    small grid: several units per workgroup, K alternating): each entry's
+    k-rows past K, for operands stored [K][N] or [K][M], end its record, so
+    no entry reads its neighbour's values."""
+    binding.set_config("BM=256,BN=256,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3")
+    batch, M, N, K = 3, 264, 520, 1000
+    say("batched ragged K", layout, (batch, M, N, K))
+    As, Bs = [], []
+    for b in range(batch):
+        A, B = synth.dense_int_operands(M, N, K, layout, seed=300 + b)
+        As.append(A)
+        Bs.append(B)
+    A_all = torch.stack(As).to(dev)
+    B_all = torch.stack(Bs).to(dev)
+    out = torch.full((batch, M, N), float("nan"), dtype=torch.float32, device=dev)
+    call_matmul_batched(A_all, B_all, batch, M, N, K, As[0].numel(), Bs[0].numel(), M * N, layout, True,
+                        out)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref, _ = oracle.gemm(synth.bits(As[b]), synth.bits(Bs[b]), layout)
+        np.testing.assert_array_equal(out[b].cpu().numpy(), ref)
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_and_tiny(dev):
     say("empty and tiny")

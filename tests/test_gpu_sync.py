@@ -193,20 +193,20 @@ def test_linear_narrow_tiles(libs, grid):
         "mm_matmul"), [out32]))
 
 
-@pytest.mark.parametrize("bn", [256, 192])
+@pytest.mark.parametrize("layout,bn", [("nt", 256), ("nt", 192), ("nn", 256), ("tn", 256), ("tt", 256)])
 @pytest.mark.parametrize("grid", [0, 5])
-def test_ragged_k(libs, bn, grid):
-    """The instance whose last super-step per tile is a partial one (K = 1000:
+def test_ragged_k(libs, layout, bn, grid):
+    """The instances whose last super-step per tile is a partial one (K = 1000:
     15 whole super-steps and 40 k more; with K alternation half the tiles
-    fetch the partial one first)."""
+    fetch the partial one first), in every operand storage."""
     dev = torch.device("cuda:0")
     M, N, K = 1040, 776, 1000
     cfg = f"BM=256,BN={bn},WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
-    A, B = operands(M, N, K, "nt", 1000 + grid, dev)
+    A, B = operands(M, N, K, layout, 1000 + grid, dev)
     bias = synth.randn_bf16((N,), 1.0, 1005).to(dev)
-    assert_slab(libs, cfg, "linear", M, N, K, "nt")
-    say("linear, ragged K", (M, N, K), cfg)
+    assert_slab(libs, cfg, "linear", M, N, K, layout)
+    say("linear, ragged K", layout, (M, N, K), cfg)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
         A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
-        binding.LAYOUTS["nt"], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))
+        binding.LAYOUTS[layout], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))
