@@ -112,12 +112,12 @@ struct KernelEntry {
   {256, 192, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 192, 2, 2, false>), {0}}
 
-// K not a multiple of 64 (single-weight products; 256 x 192 tiles for
-// K-contiguous operands only)
-#define MM_KSR(BN)                                                                         \
-  {256, BN, 2, 2, true, true, false, 3,                                                    \
+// K not a multiple of 64 (256 x 192 tiles and the FFN for K-contiguous
+// operands only)
+#define MM_KSR(BN, FFN)                                                                    \
+  {256, BN, 2, 2, true, true, FFN, 3,                                                      \
    reinterpret_cast<const void*>(                                                          \
-       &mmk::gemm_nt_slab<256, BN, 2, 2, false, false, false, false, false, false, true>), \
+       &mmk::gemm_nt_slab<256, BN, 2, 2, FFN, false, false, false, false, false, true>),   \
    {0}, false, false, false, true}
 #define MM_KSRKN(AKC, BKC)                                                                 \
   {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
@@ -161,8 +161,9 @@ KernelEntry g_kernels[] = {
     MM_KS(false),
     MM_KS(true),
     MM_KS192(),
-    MM_KSR(256),
-    MM_KSR(192),
+    MM_KSR(256, false),
+    MM_KSR(192, false),
+    MM_KSR(256, true),
     MM_KSRKN(true, false),
     MM_KSRKN(false, false),
     MM_KSRKN(false, true),
@@ -674,11 +675,11 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     // configuration (fam == c.pipe), never as another family's fallback
     if ((fam == 4 || fam == 5) && fam != c.pipe) continue;
     // the slab kernel runs super-steps of 64 k, two of them in flight; a K
-    // that is not a multiple of 64 takes its RAGGED instance (single-weight
-    // single-output products: the last super-step reads zeros past K)
+    // that is not a multiple of 64 takes its RAGGED instance (single-output
+    // products: the last super-step reads zeros past K)
     const bool ragged = fam == 3 && r.K % mmk::kSlabK != 0;
     if (fam == 3 && r.K < 2 * mmk::kSlabK) continue;
-    if (ragged && (r.ffn || r.out_pre)) continue;
+    if (ragged && r.out_pre) continue;
     // its [K][N]-weight and [K][M]-activation forms address a super-step's
     // 64 k-rows of such an operand with 32-bit buffer offsets
     if (fam == 3 && !b_kc && (int64_t)mmk::kSlabK * r.N * 2 >= (int64_t(1) << 31)) continue;

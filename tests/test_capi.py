@@ -126,8 +126,8 @@ def test_config_override_and_rejection(lib):
 def test_heuristic_choices():
     assert binding.describe_config("linear", 8192, 8192, 8192).startswith("BM=256,BN=256")
     # 256 x 256 tiles run the whole-line slab kernel when K spans two
-    # super-steps of 64 (a partial last one through the ragged instance for a
-    # single weight, the 32-k pipeline for the FFN); [K][N] weights and [K][M]
+    # super-steps of 64 (a partial last one through its ragged instances);
+    # [K][N] weights and [K][M]
     # activations (NN, TN, TT) through its transpose-read forms.  Below two
     # super-steps: the 32-k pipeline for K-contiguous operands, the basic
     # kernel for the others
@@ -137,7 +137,7 @@ def test_heuristic_choices():
     assert binding.describe_config("linear", 8192, 8192, 8200).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("linear", 8192, 8192, 136).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("linear", 8192, 8192, 120).endswith("KERNEL=gemm_nt_pipe")
-    assert binding.describe_config("ffn", 8192, 14336, 4104).endswith("KERNEL=gemm_nt_pipe")
+    assert binding.describe_config("ffn", 8192, 14336, 4104).endswith("KERNEL=gemm_nt_slab")
     assert binding.describe_config("matmul", 8192, 8192, 8192, "nn").endswith("KERNEL=gemm_nt_slab")
     for lay in ("nn", "tn", "tt"):
         assert binding.describe_config("matmul", 8192, 8192, 8200, lay).endswith("KERNEL=gemm_nt_slab")

@@ -848,6 +848,33 @@ def test_ragged_k_default_path(dev, shape):
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
+def test_ragged_k_ffn_default_path(dev):
+    """The FFN with K not a multiple of 64 on the default path: bit for bit
+    with the identity gate and integer operands (guard bands checked), SwiGLU
+    on random operands within the bf16 tolerance."""
+    M, N, K = 2000, 3000, 1000
+    cfg = binding.describe_config("ffn", M, N, K)
+    say("ragged K ffn", (M, N, K), cfg)
+    assert cfg.endswith("KERNEL=gemm_nt_slab"), cfg
+    ops = synth.mapping_operands(M, N, K, "nt", seed=77, gated=True)
+    buf, out = guarded_out(M, N, False, dev)
+    call_ffn(ops["A"].to(dev), ops["B"].to(dev), ops["B2"].to(dev), M, N, K, "identity", out)
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "glu_identity",
+                          B2=synth.bits(ops["B2"]))
+    bad = np.argwhere(to_bits(out) != bits)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    del buf, out
+    x = synth.randn_bf16((M, K), 1.0, 71)
+    Wg = synth.randn_bf16((N, K), K ** -0.5, 72)
+    Wu = synth.randn_bf16((N, K), K ** -0.5, 73)
+    got = mm.ffn_swiglu(x.to(dev), Wg.to(dev), Wu.to(dev))
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(Wg), "nt", "swiglu", B2=synth.bits(Wu))
+    assert tol_excess(got.float().cpu().numpy(), y, 2e-2) <= 0
+
+
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
 def test_ragged_k_transposed_storage(dev, layout):
     """K not a multiple of 64 with operands stored [K][N] and/or [K][M] on the

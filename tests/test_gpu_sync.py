@@ -210,3 +210,20 @@ def test_ragged_k(libs, layout, bn, grid):
     assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
         A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
         binding.LAYOUTS[layout], binding.EPILOGUES["bias_gelu_tanh"], stream()), "mm_linear"), [out]))
+
+
+@pytest.mark.parametrize("grid", [0, 7])
+def test_ffn_ragged_k(libs, grid):
+    """The FFN's ragged-K instance (gate and up rows both masked past K)."""
+    dev = torch.device("cuda:0")
+    M, N, K = 776, 1160, 1000
+    x = synth.randn_bf16((M, K), 1.0, 1010).to(dev)
+    Wg = synth.randn_bf16((N, K), K ** -0.5, 1011).to(dev)
+    Wu = synth.randn_bf16((N, K), K ** -0.5, 1012).to(dev)
+    cfg = f"BM=256,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
+    assert_slab(libs, cfg, "ffn", M, N, K, "nt")
+    say("ffn swiglu, ragged K", (M, N, K), cfg)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_ffn_swiglu(
+        x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), out.data_ptr(), M, N, K, stream()),
+        "mm_ffn_swiglu"), [out]))
