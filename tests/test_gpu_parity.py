@@ -929,6 +929,113 @@ def test_batched_ragged_k_slab(dev, layout):
         np.testing.assert_array_equal(out[b].cpu().numpy(), ref)
 
 
+# ------------------------------------------------------------ non-finite inputs
+def nonfinite_case(M, N, K, layout, seed):
+    """op(A) [M,K], op(B) [K,N] (bf16, N(0,1)-like) with +-inf and NaN entries
+    spread over several tiles and k positions: an inf above a zero of op(B)
+    (inf * 0), a NaN row, a -inf in op(B), and +inf / -inf in one row of
+    op(A).  Returns storage-layout tensors and the per-output IEEE class (0
+    finite, 1 +inf, -1 -inf, 2 NaN), which no summation order changes."""
+    a = synth.randn_bf16((M, K), 1.0, seed).float()
+    b = synth.randn_bf16((K, N), K ** -0.5, seed + 1).float()
+    inf, nan = float("inf"), float("nan")
+    for (i, k) in [(1, 2), (M - 1, K - 1), (M // 2, K // 3)]:
+        a[i, k] = inf
+    b[2, N - 1] = 0.0
+    a[min(2, M - 1), K // 2] = nan
+    b[K - 5, min(6, N - 1)] = -inf
+    b[K // 4, N // 2] = inf
+    a[min(3, M - 1), 7] = inf
+    a[min(3, M - 1), K - 8] = -inf
+    # only k positions holding a non-finite entry can make an output
+    # non-finite (the finite terms are small: no finite sum overflows)
+    ks = torch.nonzero(~torch.isfinite(a).all(0) | ~torch.isfinite(b).all(1)).flatten()
+    t = a.double()[:, ks, None] * b.double()[None, ks, :]
+    pos, neg = torch.isposinf(t).any(1), torch.isneginf(t).any(1)
+    isnan = torch.isnan(t).any(1) | (pos & neg)
+    cls = torch.where(isnan, 2, torch.where(pos, 1, torch.where(neg, -1, 0))).numpy()
+    a, b = a.to(torch.bfloat16), b.to(torch.bfloat16)
+    A = a.t().contiguous() if layout in ("tn", "tt") else a
+    B = b.t().contiguous() if layout in ("nt", "tt") else b
+    return A, B, cls
+
+
+def value_class(y):
+    y = np.asarray(y, np.float64)
+    return np.where(np.isnan(y), 2, np.where(np.isposinf(y), 1, np.where(np.isneginf(y), -1, 0)))
+
+
+# (configuration, M, N, K, layout): the slab kernel (ragged K, [K][N] weights,
+# 256 x 192 tiles), the 32-k pipeline, the all-of-K-in-LDS small kernel and
+# the basic kernel
+NONFINITE_CASES = [
+    (CONFIGS[1], 520, 395, 1032, "nt"),
+    (CONFIGS[0], 520, 392, 1024, "nn"),
+    ("BM=256,BN=192,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3", 520, 395, 1024, "nt"),
+    (CONFIGS[3], 520, 395, 1024, "nt"),
+    ("BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0,GRID=3", 300, 264, 200, "nt"),
+    ("BM=64,BN=64,WM=2,WN=2,G=3,XCD=0,KALT=0,PIPE=0", 304, 264, 200, "tn"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(NONFINITE_CASES)))
+@pytest.mark.parametrize("epi", ["none", "bias_gelu_tanh"])
+def test_nonfinite_inputs(dev, case, epi):
+    """Inf and NaN in the operands: every output has the oracle's class
+    (finite, +inf, -inf, NaN; GELU(-inf) is NaN), and the finite outputs are
+    within the bf16 tolerance."""
+    cfg, M, N, K, layout = NONFINITE_CASES[case]
+    binding.set_config(cfg)
+    say("non-finite", cfg, (M, N, K), layout, epi)
+    A, B, cls = nonfinite_case(M, N, K, layout, 31 + case)
+    bias = synth.randn_bf16((N,), 1.0, 39)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    call_linear(A.to(dev), B.to(dev), bias.to(dev), M, N, K, layout, epi, out)
+    torch.cuda.synchronize()
+    y, bits = oracle.gemm(synth.bits(A), synth.bits(B), layout, epi, bias=synth.bits(bias))
+    ref = (bits.astype(np.uint32) << 16).view(np.float32)
+    got = out.float().cpu().numpy()
+    if epi == "none":
+        np.testing.assert_array_equal(value_class(ref), cls)  # the oracle agrees with IEEE
+    np.testing.assert_array_equal(value_class(got), value_class(ref))
+    fin = value_class(ref) == 0
+    excess = np.abs(got[fin].astype(np.float64) - y[fin]) - 2e-2 * (np.abs(y[fin]) + 1.0)
+    assert excess.max() <= 0
+
+
+def test_nonfinite_inputs_split_and_ffn(dev):
+    """The same classes through split-K (partial tiles added by the
+    reduction) and through the FFN's SwiGLU (SiLU(-inf) u is NaN)."""
+    M, N, K = 520, 392, 8192
+    A, B, cls = nonfinite_case(M, N, K, "nt", 41)
+    assert binding.workspace_size("matmul", M, N, K, "nt") > 0, "shape no longer split"
+    ws = torch.empty(binding.workspace_size("matmul", M, N, K, "nt"), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    say("non-finite split-K", (M, N, K))
+    mm.matmul(A.to(dev), B.to(dev).t(), torch.float32, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    y, _ = oracle.gemm(synth.bits(A), synth.bits(B), "nt")
+    np.testing.assert_array_equal(value_class(y), cls)
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(value_class(got), cls)
+    fin = cls == 0
+    assert tol_excess(got[fin], y[fin], 1e-3) <= 0
+    M, N, K = 300, 264, 1032
+    x, Wg, _ = nonfinite_case(M, N, K, "nt", 43)
+    Wu = synth.randn_bf16((N, K), K ** -0.5, 45)
+    Wu[5, :] = 0.0  # SiLU(+-inf) * 0 = NaN as well
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    say("non-finite ffn", (M, N, K))
+    mm.ffn_swiglu(x.to(dev), Wg.to(dev), Wu.to(dev), out=out)
+    torch.cuda.synchronize()
+    y, bits = oracle.gemm(synth.bits(x), synth.bits(Wg), "nt", "swiglu", B2=synth.bits(Wu))
+    ref = (bits.astype(np.uint32) << 16).view(np.float32)
+    got = out.float().cpu().numpy()
+    np.testing.assert_array_equal(value_class(got), value_class(ref))
+    fin = value_class(ref) == 0
+    assert tol_excess(got[fin], y[fin], 2e-2) <= 0
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_and_tiny(dev):
     say("empty and tiny")

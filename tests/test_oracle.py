@@ -388,3 +388,76 @@ def test_empty_sum_gives_the_epilogue_of_the_bias():
     for epi in ("swiglu", "glu_identity"):
         y, _ = oracle.gemm(A, B, "nt", epi, B2=B)
         assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------- non-finite inputs
+def nonfinite_operands(M, N, K, seed):
+    """op(A) [M,K], op(B) [K,N] bf16 bits: N(0,1)-like values with a few +-inf
+    and NaN entries, and a zero of op(B) under an inf of op(A)."""
+    a = bits_to_f32(rand_bits((M, K), seed)).copy()
+    b = bits_to_f32(rand_bits((K, N), seed + 1)).copy()
+    a[1, 2] = np.inf       # row 1: +-inf by the sign of b[2, j] ...
+    b[2, 3] = 0.0          # ... and inf * 0 = NaN at (1, 3)
+    a[2, 4] = np.nan       # row 2: NaN throughout
+    b[5, 6] = -np.inf      # column 6: +-inf by the sign of a[i, 5]
+    a[3, 7] = np.inf       # row 3: +inf and -inf terms where b[7, j] and
+    a[3, 8] = -np.inf      # b[8, j] share a sign: NaN there
+    return f32_to_bits(a), f32_to_bits(b)
+
+
+def ieee_class(a, b):
+    """Class of each entry of a @ b in any summation order: 0 finite, 1 +inf,
+    -1 -inf, 2 NaN (terms NaN, inf * 0, or +inf and -inf together).  Finite
+    terms are small, so no finite sum overflows."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        t = a.astype(np.float64)[:, :, None] * b.astype(np.float64)[None, :, :]
+    nan = np.isnan(t).any(1) | (np.isposinf(t).any(1) & np.isneginf(t).any(1))
+    out = np.where(np.isposinf(t).any(1), 1, np.where(np.isneginf(t).any(1), -1, 0))
+    return np.where(nan, 2, out)
+
+
+def value_class(y):
+    y = np.asarray(y, np.float64)
+    return np.where(np.isnan(y), 2, np.where(np.isposinf(y), 1, np.where(np.isneginf(y), -1, 0)))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_nonfinite_inputs_follow_ieee(layout):
+    """Inf and NaN inputs: every output's class (finite, +inf, -inf, NaN) is
+    the one IEEE arithmetic fixes whatever the summation order, in the fp32
+    result and in its bf16 bits; finite outputs match float64 within the
+    fp32 accumulation bound."""
+    M, N, K = 9, 11, 16
+    ab, bb = nonfinite_operands(M, N, K, 21)
+    a, b = bits_to_f32(ab), bits_to_f32(bb)
+    A, B = store(ab, bb, layout)
+    y, bits = oracle.gemm(A, B, layout)
+    cls = ieee_class(a, b)
+    assert {0, 1, -1, 2} <= set(np.unique(cls).tolist()), "the case should hold every class"
+    np.testing.assert_array_equal(value_class(y), cls)
+    np.testing.assert_array_equal(value_class(bits_to_f32(bits)), cls)
+    fin = cls == 0
+    with np.errstate(invalid="ignore"):
+        ref = a.astype(np.float64) @ b.astype(np.float64)
+        bound = 2 * K * np.finfo(np.float32).eps * (np.abs(a).astype(np.float64) @ np.abs(b)) + 1e-30
+    assert np.all(np.abs(y[fin] - ref[fin]) <= bound[fin])
+
+
+def test_nonfinite_through_the_epilogues():
+    """GELU(+inf) = +inf, GELU(-inf) = NaN (the tanh form is -inf * 0 there),
+    GELU(NaN) = NaN; SiLU(g) u and g u follow IEEE products."""
+    t = np.array([np.inf, -np.inf, np.nan, 3.0], np.float32)
+    g = oracle.gelu_tanh(t)
+    assert g[0] == np.inf and np.isnan(g[1]) and np.isnan(g[2]) and np.isfinite(g[3])
+    # through the full epilogue: a 1 x 4 output with K = 1, op(A) = [1], op(B) = t
+    ones = f32_to_bits(np.ones((1, 1), np.float32))
+    tb = f32_to_bits(t.reshape(1, 4))
+    bias = f32_to_bits(np.zeros(4, np.float32))
+    y, _ = oracle.gemm(ones, tb, "nn", "bias_gelu_tanh", bias=bias)
+    assert y[0, 0] == np.inf and np.isnan(y[0, 1]) and np.isnan(y[0, 2])
+    u = f32_to_bits(np.array([[2.0, 2.0, 2.0, 0.0]], np.float32))
+    y, _ = oracle.gemm(ones, tb, "nn", "glu_identity", B2=u)
+    assert y[0, 0] == np.inf and y[0, 1] == -np.inf and np.isnan(y[0, 2]) and y[0, 3] == 0.0
+    y, _ = oracle.gemm(ones, tb, "nn", "swiglu", B2=u)
+    # SiLU(+inf) = +inf, SiLU(-inf) = -inf / (1 + inf) = NaN
+    assert y[0, 0] == np.inf and np.isnan(y[0, 1]) and np.isnan(y[0, 2])
