@@ -8,8 +8,9 @@ program's own (the outputs are overwritten, other kernels run, the host
 synchronizes), and every replay is checked, not just the first.  The cases
 cover the slab kernel with a fused epilogue, the horizontally fused FFN, and
 split-K with its two launches, through a caller's workspace and through the
-library's static scratch, and a split linear form whose reduction applies
-the epilogue.
+library's static scratch, a split linear form whose reduction applies
+the epilogue, and a K that is not a multiple of 64 (the slab kernel's
+ragged instance).
 """
 
 import pytest
@@ -65,7 +66,14 @@ def test_graph_replays_equal_eager_calls(dev):
     # the same split with the linear form's epilogue, applied by the reduction
     bias_s = synth.randn_bf16((Ns,), 1.0, 809).to(dev)
     y5 = torch.empty((Ms, Ns), dtype=torch.bfloat16, device=dev)
-    outs = (y1, y2, y3, y4, y5)
+    # K = 1032: every tile's last super-step is a partial one
+    Mr, Nr, Kr = 2900, 3000, 1032
+    assert binding.describe_config("linear", Mr, Nr, Kr).endswith("KERNEL=gemm_nt_slab")
+    xr = synth.randn_bf16((Mr, Kr), 1.0, 810).to(dev)
+    Wr = synth.randn_bf16((Nr, Kr), Kr ** -0.5, 811).to(dev)
+    br = synth.randn_bf16((Nr,), 1.0, 812).to(dev)
+    y6 = torch.empty((Mr, Nr), dtype=torch.bfloat16, device=dev)
+    outs = (y1, y2, y3, y4, y5, y6)
 
     def calls():
         mm.linear(x, W, bias, "bias_gelu_tanh", out=y1)
@@ -73,6 +81,7 @@ def test_graph_replays_equal_eager_calls(dev):
         mm.matmul(As, Bs.t(), torch.float32, out=y3, workspace=ws)
         noalloc(As, Bs, Ms, Ns, Ks, y4)
         mm.linear(As, Bs, bias_s, "bias_gelu_tanh", out=y5, workspace=ws)
+        mm.linear(xr, Wr, br, "bias_gelu_tanh", out=y6)
 
     calls()
     torch.cuda.synchronize()

@@ -49,9 +49,11 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 # (M, N, K, layout): two calls in a row, the second smaller, both split by the
 # automatic rule (20 tiles of 256 x 192 in 8 chunks: 160 slots = 40 MiB of
 # scratch; then 9 tiles in 4 chunks: 36 slots); then a stored-[K][N] product
-# (256 x 256 tiles) and a shape that runs unsplit
+# (256 x 256 tiles), a shape that runs unsplit, and one whose K is not a
+# multiple of 64 (never split: the slab kernel's ragged instance)
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
-            (520, 392, 512, "nt")]
+            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt")]
+UNSPLIT = {(520, 392, 512), (2900, 3000, 1032)}
 
 
 @pytest.mark.parametrize("out_f32", [True, False])
@@ -66,7 +68,7 @@ def test_noalloc_matches_workspace_entry_point(dev, out_f32):
         noalloc(Ad, Bd, M, N, K, layout, out_f32, got)
         torch.cuda.synchronize()
         nbytes = with_ws(Ad, Bd, M, N, K, layout, out_f32, want)
-        if (M, N, K) != (520, 392, 512):
+        if (M, N, K) not in UNSPLIT:
             assert nbytes > 0, "this shape should take the split-K path"
         # same kernels, same partial sums, same order: identical bits
         assert torch.equal(got.view(torch.int32 if out_f32 else torch.int16),
