@@ -194,8 +194,7 @@ gemm_nt_slab(GemmParams p) {
   // tail_bits); an operand stored [K][N] or [K][M] needs nothing: its k-rows
   // past K lie past the end of the matrix, outside the record, and read as
   // zeros too.
-  static_assert(!(RAGGED && (SPLITK || PRE || BSTAGE || (FFN && (BKN || AMK)))),
-                "ragged K: single-output forms");
+  static_assert(!(RAGGED && (PRE || BSTAGE || (FFN && (BKN || AMK)))), "ragged K: single-output forms");
   // PRE: the instance that also stores the pre-activation (p.out_pre).  It is
   // a separate instance because any extra epilogue path in the default one
   // changes the register allocation of its K loop.

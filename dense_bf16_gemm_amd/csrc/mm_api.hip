@@ -96,6 +96,19 @@ struct KernelEntry {
        &mmk::gemm_nt_slab<256, 192, 2, 2, false, true, false, false, false, false>),       \
    {0}, true}
 
+// the same pieces for a K that is not a multiple of 64 (the chunk holding the
+// last super-step masks its partial copies)
+#define MM_KSKR(AKC, BKC)                                                                  \
+  {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, !(BKC), !(AKC), false, true>), \
+   {0}, true, false, false, true}
+#define MM_KSK192R()                                                                       \
+  {256, 192, 2, 2, true, true, false, 3,                                                   \
+   reinterpret_cast<const void*>(                                                          \
+       &mmk::gemm_nt_slab<256, 192, 2, 2, false, true, false, false, false, false, true>), \
+   {0}, true, false, false, true}
+
 #define MM_KSP()                                                                           \
   {256, 256, 2, 2, true, true, false, 3,                                                   \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, true>), {0}, \
@@ -154,6 +167,11 @@ KernelEntry g_kernels[] = {
     MM_KSK(false, false),
     MM_KSK(false, true),
     MM_KSK192(),
+    MM_KSKR(true, true),
+    MM_KSKR(true, false),
+    MM_KSKR(false, false),
+    MM_KSKR(false, true),
+    MM_KSK192R(),
     MM_KSP(),
     MM_KSB(),
     MM_KWS(),
@@ -532,11 +550,12 @@ bool b_kcontig(int layout) { return layout == MM_NT || layout == MM_TT; }
 
 // single-output products of one weight (plain or linear; the reduction
 // applies the bias and GELU to the summed value) in the slab kernel's domain:
-// whole super-steps, and 32-bit offsets within a tile's K-contiguous rows and
-// a super-step's k-rows of an operand stored [K][M] / [K][N]
+// at least two super-steps (the last may be partial), and 32-bit offsets
+// within a tile's K-contiguous rows and a super-step's k-rows of an operand
+// stored [K][M] / [K][N]
 bool splitk_shape(const Request& r) {
-  return r.batch == 1 && !r.ffn && !r.out_pre && r.K % mmk::kSlabK == 0 &&
-         r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31) &&
+  return r.batch == 1 && !r.ffn && !r.out_pre && r.K >= 2 * mmk::kSlabK &&
+         (int64_t)256 * r.K * 2 < (int64_t(1) << 31) &&
          (a_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.M * 2 < (int64_t(1) << 31)) &&
          (b_kcontig(r.layout) || (int64_t)mmk::kSlabK * r.N * 2 < (int64_t(1) << 31));
 }
@@ -562,7 +581,7 @@ SkPlan splitk_plan_bn(const Request& r, const Config& c, int64_t wgs, int bn) {
   sp.bn = bn;
   if (c.sk == 1 || !splitk_shape(r) || wgs > kSkMaxWgs) return sp;
   const int64_t T = cdiv(r.M, 256) * cdiv(r.N, bn);
-  const int64_t KS = r.K / mmk::kSlabK;
+  const int64_t KS = cdiv(r.K, mmk::kSlabK);
   int n;
   if (c.sk >= 2) {
     n = c.sk;
@@ -636,7 +655,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     c.bm = 256;
     c.bn = sp.bn;
     c.wgm = c.wgn = 2;
-    k = find_kernel(256, sp.bn, 2, 2, a_kc, b_kc, false, 3, true);
+    k = find_kernel(256, sp.bn, 2, 2, a_kc, b_kc, false, 3, true, false, false, r.K % mmk::kSlabK != 0);
   }
   // the wave-specialized kernel (a configuration override for comparison)
   // takes single-weight K-contiguous products with whole super-steps; other

@@ -153,15 +153,16 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
 
 /* Split-K workspace (PR "Implement persistent matmul scheduling", review
  * notes: splitting the K loop over workgroups, split-K and stream-K, named
- * there and left out of the persistent scheduler).  When a plain product --
- * mm_matmul, or mm_linear with MM_EPI_NONE, any layout -- with K a
- * multiple of 64 has fewer 256 x 256 output tiles than the GPU has resident
- * workgroups (at most half as many) and K long enough that each chunk spans
- * at least 8 x 64 of it, the _ws entry points below cut each tile's K loop into chunks
- * and deal the chunks of all tiles to the resident workgroups (one chunk
- * each, or equal contiguous ranges: stream-K); each piece leaves its fp32
- * partial tile in this workspace (one 256 KiB slot per workgroup, two per
- * stream-K workgroup), and a second kernel on the same stream adds them.
+ * there and left out of the persistent scheduler).  When a single-weight
+ * product -- mm_matmul, or mm_linear with any epilogue, any layout, K >= 128
+ * -- has fewer 256 x 256 (or 256 x 192) output tiles than the GPU has
+ * resident workgroups (at most half as many) and K long enough that each
+ * chunk spans at least 32 x 64 of it, the _ws entry points below cut each
+ * tile's K loop into chunks and deal the chunks of all tiles to the resident
+ * workgroups (one chunk each, or equal contiguous ranges: stream-K); each
+ * piece leaves its fp32 partial tile in this workspace (one 256 KiB slot per
+ * workgroup, two per stream-K workgroup), and a second kernel on the same
+ * stream adds them in k order and applies the epilogue once.
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
  *   bytes   receives the size a call of this shape on the current device may
  *           use; 0 = the shape runs without one.  Queries the device (CU

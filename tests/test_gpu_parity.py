@@ -353,9 +353,13 @@ def test_preact_random_matches_single_output(dev, epi):
 # (M, N, K, config): automatic chunk-major (16 chunks per tile, one per
 # workgroup); forced stream-K on 140 tiles (ranges of 3/4 of a tile);
 # ranges of two chunks of three that cross tile boundaries; ranges of
-# three of four; uneven chunk-major chunks (64 super-steps in 7)
+# three of four; uneven chunk-major chunks (64 super-steps in 7); and K not a
+# multiple of 64 (the last chunk of each tile ends with a partial super-step),
+# chunk-major and in stream-K ranges
 SK_CASES = [
     (520, 395, 8192, None),
+    (520, 395, 8200, None),
+    (300, 264, 2056, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6"),
     (2560, 3584, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=4"),
     (300, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6"),
     (257, 520, 1024, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=0,KALT=2,SK=4,GRID=10"),
@@ -401,7 +405,7 @@ def test_splitk_mapping_bitexact(dev, case, out_f32):
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
-@pytest.mark.parametrize("case", [(520, 392, 8192, None),
+@pytest.mark.parametrize("case", [(520, 392, 8192, None), (520, 392, 8200, None),
                                   (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
 def test_splitk_mapping_layouts(dev, layout, case):
     """Split-K (chunk-major, and stream-K ranges across tile boundaries) with
@@ -498,7 +502,7 @@ def test_splitk_auto_workspace_two_streams(dev):
         assert not any(k[0] == dev.index for k in gemm_mod._workspaces)
 
 
-@pytest.mark.parametrize("case", [(520, 395, 8192, None),
+@pytest.mark.parametrize("case", [(520, 395, 8192, None), (520, 395, 8200, None),
                                   (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
 def test_splitk_linear_epilogues(dev, case):
     """Split-K of the linear form: the reduction adds the pieces in k order,
@@ -1295,6 +1299,7 @@ def test_splitk_tile_width_choice(dev):
     if torch.cuda.get_device_properties(dev).multi_processor_count != 256:
         pytest.skip("the choice is stated for a 256-CU GPU")
     assert ",SPLIT=2x192," in binding.describe_config("matmul", 2047, 3001, 65536)
+    assert ",SPLIT=2x192," in binding.describe_config("matmul", 2047, 3001, 65544)  # ragged K
     assert ",SPLIT=2x256," in binding.describe_config("matmul", 2047, 3001, 65536, "nn")
     binding.set_config("BM=256,BN=256,WM=2,WN=2,G=4,XCD=1,KALT=2,PIPE=3")
     try:

@@ -130,7 +130,7 @@ def test_ffn_and_preact(libs, grid):
 
 
 @pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
-@pytest.mark.parametrize("case", [(520, 392, 8192, None),
+@pytest.mark.parametrize("case", [(520, 392, 8192, None), (520, 392, 8200, None),
                                   (304, 264, 2048, "BM=256,BN=256,WM=2,WN=2,G=8,XCD=1,KALT=2,SK=3,GRID=6")])
 def test_splitk(libs, layout, case):
     dev = torch.device("cuda:0")
