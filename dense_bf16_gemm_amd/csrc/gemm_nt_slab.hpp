@@ -86,10 +86,18 @@ __device__ __forceinline__ void gelu_tanh8(float (&v)[8]) {
 // the three free issue slots after each of the row's eight MFMAs.
 // 0x008: MFMA, 0x006: scalar or vector ALU, 0x020: memory read (the copy),
 // 0x100: LDS read.
-// MPR: MFMAs per row (8 for a 128-column wave block, 6 for 96 columns).
+// MPR: MFMAs per row (8 for a 128-column wave block, 6 for 96 columns, 4 for
+// 64).
 template <int MPR>
 __device__ __forceinline__ void spread_first_row_a() {
-  if constexpr (MPR == 8) {
+  if constexpr (MPR == 4) {
+    // (four MFMAs for the same scalar chain: it overflows the free slots)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 6, 0);
+    }
+  } else if constexpr (MPR == 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -101,7 +109,7 @@ __device__ __forceinline__ void spread_first_row_a() {
       __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
     }
   } else {
-    static_assert(MPR == 6, "rows of 8 or 6 MFMAs");
+    static_assert(MPR == 6, "rows of 8, 6 or 4 MFMAs");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -118,6 +126,19 @@ __device__ __forceinline__ void spread_first_row_a() {
 }
 template <int MPR>
 __device__ __forceinline__ void spread_first_row_b() {
+  if constexpr (MPR == 4) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 5, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    return;
+  }
   constexpr int lead = MPR == 8 ? 3 : 2;
 #pragma unroll
   for (int i = 0; i < lead; ++i) {
@@ -206,14 +227,16 @@ gemm_nt_slab(GemmParams p) {
   constexpr int FN = WTN / 16;
   constexpr int OUT_BN = FFN ? BN / 2 : BN;
   constexpr int UNIT = 256 * kSlabRowB;  // 32 KiB
-  // BN = 192 (a 128 x 96 block per wave): K-contiguous single-weight products
-  // whose 256 x 256 tiles would leave much of the grid idle (split or not)
-  static_assert(BM == 256 && (BN == 256 || (BN == 192 && !BKN && !AMK && !FFN && !PRE && !BSTAGE)) &&
+  // BN = 192 or 128 (a 128 x 96 or 128 x 64 block per wave): K-contiguous
+  // single-weight products whose 256 x 256 tiles would leave much of the grid
+  // idle (split or not); the weight slab then fills 3/4 or 1/2 of its unit
+  static_assert(BM == 256 &&
+                    (BN == 256 || ((BN == 192 || BN == 128) && !BKN && !AMK && !FFN && !PRE && !BSTAGE)) &&
                     NW == 4,
                 "a unit holds 256 rows; four waves");
-  static_assert(FM == 8 && (FN == 8 || FN == 6), "row schedule assumes 8 x 8 (or 8 x 6) fragments per wave");
+  static_assert(FM == 8 && (FN == 8 || FN == 6 || FN == 4), "row schedule assumes 8 x 8, 8 x 6 or 8 x 4 fragments per wave");
   constexpr int CPS = BM / 8 / NW;     // 1 KiB activation copies per wave per slab
-  constexpr int CPS_B = BN / 8 / NW;   // weight copies (as many, or 6 for BN = 192)
+  constexpr int CPS_B = BN / 8 / NW;   // weight copies (as many, or 6 / 4 for BN = 192 / 128)
   static_assert(CPS == FM, "one activation copy per MFMA row");
 
   __shared__ __attribute__((aligned(1024))) char smem[kSlabUnits * UNIT];

@@ -88,12 +88,12 @@ struct KernelEntry {
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, !(BKC), !(AKC)>), \
    {0}, true}
 
-// split-K pieces on 256 x 192 tiles (K-contiguous operands): for products
-// whose 256 x 256 tiles, split, would leave a quarter or more of the grid idle
-#define MM_KSK192()                                                                        \
-  {256, 192, 2, 2, true, true, false, 3,                                                   \
+// split-K pieces on 256 x 192 or 256 x 128 tiles (K-contiguous operands): for
+// products whose 256 x 256 tiles, split, would leave much of the grid idle
+#define MM_KSKW(BN)                                                                        \
+  {256, BN, 2, 2, true, true, false, 3,                                                    \
    reinterpret_cast<const void*>(                                                          \
-       &mmk::gemm_nt_slab<256, 192, 2, 2, false, true, false, false, false, false>),       \
+       &mmk::gemm_nt_slab<256, BN, 2, 2, false, true, false, false, false, false>),        \
    {0}, true}
 
 // the same pieces for a K that is not a multiple of 64 (the chunk holding the
@@ -103,10 +103,10 @@ struct KernelEntry {
    reinterpret_cast<const void*>(                                                          \
        &mmk::gemm_nt_slab<256, 256, 2, 2, false, true, false, !(BKC), !(AKC), false, true>), \
    {0}, true, false, false, true}
-#define MM_KSK192R()                                                                       \
-  {256, 192, 2, 2, true, true, false, 3,                                                   \
+#define MM_KSKWR(BN)                                                                       \
+  {256, BN, 2, 2, true, true, false, 3,                                                    \
    reinterpret_cast<const void*>(                                                          \
-       &mmk::gemm_nt_slab<256, 192, 2, 2, false, true, false, false, false, false, true>), \
+       &mmk::gemm_nt_slab<256, BN, 2, 2, false, true, false, false, false, false, true>),  \
    {0}, true, false, false, true}
 
 #define MM_KSP()                                                                           \
@@ -120,13 +120,14 @@ struct KernelEntry {
   {256, 256, 2, 2, AKC, BKC, false, 3,                                                     \
    reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 256, 2, 2, false, false, false, !(BKC), !(AKC)>), {0}}
 
-// the single-weight linear / plain form on 256 x 192 tiles (K-contiguous)
-#define MM_KS192()                                                                         \
-  {256, 192, 2, 2, true, true, false, 3,                                                   \
-   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, 192, 2, 2, false>), {0}}
+// the single-weight linear / plain form on 256 x 192 or 256 x 128 tiles
+// (K-contiguous)
+#define MM_KSW(BN)                                                                         \
+  {256, BN, 2, 2, true, true, false, 3,                                                    \
+   reinterpret_cast<const void*>(&mmk::gemm_nt_slab<256, BN, 2, 2, false>), {0}}
 
-// K not a multiple of 64 (256 x 192 tiles and the FFN for K-contiguous
-// operands only)
+// K not a multiple of 64 (256 x 192 / 256 x 128 tiles and the FFN for
+// K-contiguous operands only)
 #define MM_KSR(BN, FFN)                                                                    \
   {256, BN, 2, 2, true, true, FFN, 3,                                                      \
    reinterpret_cast<const void*>(                                                          \
@@ -166,21 +167,25 @@ KernelEntry g_kernels[] = {
     MM_KSK(true, false),
     MM_KSK(false, false),
     MM_KSK(false, true),
-    MM_KSK192(),
+    MM_KSKW(192),
+    MM_KSKW(128),
     MM_KSKR(true, true),
     MM_KSKR(true, false),
     MM_KSKR(false, false),
     MM_KSKR(false, true),
-    MM_KSK192R(),
+    MM_KSKWR(192),
+    MM_KSKWR(128),
     MM_KSP(),
     MM_KSB(),
     MM_KWS(),
     MM_KPPT(),
     MM_KS(false),
     MM_KS(true),
-    MM_KS192(),
+    MM_KSW(192),
+    MM_KSW(128),
     MM_KSR(256, false),
     MM_KSR(192, false),
+    MM_KSR(128, false),
     MM_KSR(256, true),
     MM_KSRKN(true, false),
     MM_KSRKN(false, false),
@@ -548,6 +553,64 @@ constexpr int64_t kSkMaxWgs = 1024;  // bounds the workspace (at most 512 MiB)
 bool a_kcontig(int layout) { return layout == MM_NN || layout == MM_NT; }
 bool b_kcontig(int layout) { return layout == MM_NT || layout == MM_TT; }
 
+// ----------------------------------------------------------------------------
+// Cost model of the automatic tile and split choices.  Unit: one 64-k
+// super-step of 256 x 256 slab tiles on a full grid.  Per-tile costs measured
+// on one pass of 256 tiles at K = 2048 and 4096 (linear + bias + GELU, one
+// box): a 256 x 192 slab tile 0.79 of a 256 x 256 one, 256 x 128 0.60, a
+// 128 x 128 tile of the 32-k pipeline 0.46.  A pass with part of the grid
+// idle runs its tiles faster (under the power limit the busy CUs clock
+// higher): modelled as 0.6 + 0.4 x the busy fraction (2048^3 on 128 tiles of
+// 256 x 128: 23.7-24.7 us against 33.5 for a full pass of them).  A split
+// adds its partial tiles' write and read and the output's write at ~5 TB/s:
+// one unit (~1.25 us) per 6.25 MB.
+// ----------------------------------------------------------------------------
+enum TileKind { kTile256 = 0, kTile192 = 1, kTile128 = 2, kPipe128 = 3 };
+constexpr double kTileCost[] = {1.0, 0.79, 0.60, 0.46};
+constexpr int64_t kModelGrid = 256;          // CUs of the target GPU
+constexpr double kBytesPerUnit = 6.25e6;
+
+double pass_units(int64_t tiles) {
+  const int64_t full = tiles / kModelGrid, rem = tiles % kModelGrid;
+  return (double)full + (rem ? 0.6 + 0.4 * (double)rem / (double)kModelGrid : 0.0);
+}
+
+int64_t kind_tiles(const Request& r, int kind) {
+  switch (kind) {
+    case kTile256: return cdiv(r.M, 256) * cdiv(r.N, 256);
+    case kTile192: return cdiv(r.M, 256) * cdiv(r.N, 192);
+    case kTile128: return cdiv(r.M, 256) * cdiv(r.N, 128);
+    default: return cdiv(r.M, 128) * cdiv(r.N, 128);
+  }
+}
+
+double unsplit_cost(const Request& r, int kind) {
+  return kTileCost[kind] * pass_units(kind_tiles(r, kind)) * (double)cdiv(r.K, mmk::kSlabK);
+}
+
+// the narrower slab tiles and the 128 x 128 pipeline: K-contiguous
+// single-weight single-output products of at least two super-steps
+bool narrow_eligible(const Request& r) {
+  return a_kcontig(r.layout) && b_kcontig(r.layout) && !r.ffn && !r.out_pre && r.batch == 1 &&
+         r.K >= 2 * mmk::kSlabK && (int64_t)256 * r.K * 2 < (int64_t(1) << 31);
+}
+
+// the cheapest unsplit tile kind for a request (256 x 256 when only that runs)
+int best_unsplit_kind(const Request& r, double* cost) {
+  int best = kTile256;
+  double bc = unsplit_cost(r, kTile256);
+  if (narrow_eligible(r))
+    for (int kind = kTile192; kind <= kPipe128; ++kind) {
+      const double c = unsplit_cost(r, kind);
+      if (c < bc) {
+        bc = c;
+        best = kind;
+      }
+    }
+  if (cost) *cost = bc;
+  return best;
+}
+
 // single-output products of one weight (plain or linear; the reduction
 // applies the bias and GELU to the summed value) in the slab kernel's domain:
 // at least two super-steps (the last may be partial), and 32-bit offsets
@@ -564,7 +627,7 @@ struct SkPlan {
   int n = 1;        // chunks per tile (1 = no split)
   int q = 0;        // chunks per workgroup range; 0 = chunk-major, one per workgroup
   int64_t wgs = 0;  // workgroups with work (the grid)
-  int bn = 256;     // tile width: 256, or 192 (K-contiguous operands)
+  int bn = 256;     // tile width: 256, or 192 / 128 (K-contiguous operands)
 };
 
 // Chunks and their dealing for `wgs` resident workgroups.  Automatic: only
@@ -615,16 +678,43 @@ SkPlan splitk_plan_bn(const Request& r, const Config& c, int64_t wgs, int bn) {
   return sp;
 }
 
-// The automatic split takes 256 x 192 tiles (K-contiguous operands) when they
-// occupy more of the grid than 256 x 256 tiles: the 2047 x 3001 x 65536 fp32
-// matmul has 96 tiles of 256 x 256 (2 chunks each: 192 of 256 workgroups) or
-// 128 of 256 x 192 (2 chunks: all 256).  A forced configuration keeps 256.
+// The automatic split weighs every chunk-major plan -- tile width 256, and
+// 192 or 128 for K-contiguous operands; 2 to 16 chunks per tile, each of at
+// least 8 super-steps, all chunks resident at once -- by the cost model
+// against the cheapest unsplit run, and takes the cheapest, or none.  The
+// 2047 x 3001 x 65536 fp32 matmul splits in 2 on 128 tiles of 256 x 192 (all
+// 256 CUs; 96 tiles of 256 x 256 in 2 chunks would leave 64 idle);
+// 1024 x 4096 x 4096 stays unsplit (38.8-42.6 us; split in 2 on 256 x 256 or
+// 256 x 192 tiles, 55 us), and so does every K below ~2048 at these sizes (the
+// pieces' partial tiles cost more than the fuller grid gains).  A forced
+// configuration (or chunk count) keeps 256 x 256 tiles and the rule of
+// splitk_plan_bn.
 SkPlan splitk_plan(const Request& r, const Config& c, int64_t wgs) {
-  SkPlan a = splitk_plan_bn(r, c, wgs, 256);
-  if (c.forced || !(a_kcontig(r.layout) && b_kcontig(r.layout))) return a;
-  SkPlan b = splitk_plan_bn(r, c, wgs, 192);
-  if (b.n > 1 && b.q == 0 && (a.n <= 1 || (a.q == 0 && b.wgs > a.wgs))) return b;
-  return a;
+  if (c.forced || c.sk >= 2) return splitk_plan_bn(r, c, wgs, 256);
+  SkPlan best;  // n = 1: no split
+  if (c.sk == 1 || !splitk_shape(r) || wgs > kSkMaxWgs) return best;
+  double best_cost = 0.0;
+  best_unsplit_kind(r, &best_cost);
+  const int64_t KS = cdiv(r.K, mmk::kSlabK);
+  const int widths[] = {256, 192, 128};
+  for (int i = 0; i < 3; ++i) {
+    if (i > 0 && !narrow_eligible(r)) break;
+    const int bn = widths[i];
+    const int64_t T = cdiv(r.M, 256) * cdiv(r.N, bn);
+    for (int n = 2; n <= 16 && n * T <= wgs && KS / n >= 8; ++n) {
+      const double bytes = 2.0 * (double)(n * T) * 256.0 * bn * 4.0 +
+                           (double)r.M * (double)r.N * (r.out_f32 ? 4.0 : 2.0);
+      const double cost = kTileCost[i] * pass_units(n * T) * (double)cdiv(KS, n) + bytes / kBytesPerUnit;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best.n = n;
+        best.q = 0;
+        best.wgs = n * T;
+        best.bn = bn;
+      }
+    }
+  }
+  return best;
 }
 
 // one slot per chunk-major workgroup; two per stream-K workgroup (its range
@@ -674,10 +764,11 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   if (!sk && !r.ffn && c.bm == 64 && c.bn == 64 && c.wgm == 2 && c.wgn == 2 && c.pipe != 0 &&
       r.K <= mmk::kSmallKMax)
     k = find_kernel(64, 64, 2, 2, a_kc, b_kc, false, 6);
-  // 256 x 192 tiles exist for the slab kernel's K-contiguous single-weight
-  // single-output form only; other requests under such a configuration run
-  // 256 x 256 tiles
-  if (!sk && c.bn == 192 &&
+  // 256 x 192 and 256 x 128 slab tiles exist for the K-contiguous
+  // single-weight single-output form only; other requests under such a
+  // configuration run 256 x 256 tiles
+  const bool narrow = c.bn == 192 || (c.bm == 256 && c.bn == 128 && c.wgm == 2 && c.wgn == 2 && c.pipe == 3);
+  if (!sk && narrow &&
       !(a_kc && b_kc && !r.ffn && !r.out_pre && r.K >= 2 * mmk::kSlabK &&
         (int64_t)256 * r.K * 2 < (int64_t(1) << 31))) {
     c.bm = c.bn = 256;
@@ -705,7 +796,7 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
     if (fam == 3 && !a_kc && (int64_t)mmk::kSlabK * r.M * 2 >= (int64_t(1) << 31)) continue;
     // the bias-staging instance: K-contiguous single-weight linear forms
     // with a bias epilogue, when the configuration asks for it
-    const bool bstage = fam == 3 && c.bstage && a_kc && b_kc && !r.ffn && !r.out_pre && r.batch == 1 &&
+    const bool bstage = fam == 3 && c.bstage && c.bn == 256 && a_kc && b_kc && !r.ffn && !r.out_pre && r.batch == 1 &&
                         !ragged && (r.epi == mmk::EPI_BIAS || r.epi == mmk::EPI_BIAS_GELU);
     k = find_kernel(c.bm, c.bn, c.wgm, c.wgn, a_kc, b_kc, r.ffn, fam, false, fam == 3 && r.out_pre, bstage,
                     ragged);
@@ -765,25 +856,24 @@ mm_status plan_host(const Request& r, const Config& c_in, Plan* pl, const SkPlan
   return MM_OK;
 }
 
-// The heuristic's configuration for a request: its 256 x 256 tiles become
-// 256 x 192 for a K-contiguous single-weight product when that takes fewer
-// passes of a 256-CU grid, weighed by the narrower tile's cost (a 256 x 192
-// super-step of operands served by the Infinity Cache took ~1760 cycles
-// against ~2246 for 256 x 256: 0.78 of the time for 0.75 of the work).
-// 6144^3 (576 tiles, 2.25 passes) and 3072^3 (144 tiles, half the CUs idle)
-// take it; 8192^3 (4 passes against 6) does not.  A forced configuration is
-// kept as it is.
+// The heuristic's configuration for a request, refined by the cost model for
+// K-contiguous single-weight products where the heuristic picked 256 x 256 or
+// 128 x 128 tiles: the cheapest of 256 x 256, 256 x 192 and 256 x 128 slab
+// tiles and 128 x 128 pipeline tiles.  8192^3 and 4096^3 keep 256 x 256
+// (full passes), 6144^3 and 3072^3 take 256 x 192 (3 full passes against
+// 2.25; 192 tiles against 144), 2560^3 and 2048^3 256 x 128 (200 and 128
+// tiles: 51.2 -> 33.4 us and 26.2 -> 24.7 us against 128 x 128 pipeline
+// tiles).  A forced configuration is kept as it is.
 Config choose_config_for(const Request& r) {
   Config c = choose_config(r.ffn, r.M, r.N, r.K);
-  if (c.forced || c.bm != 256 || c.bn != 256 || c.wgm != 2 || c.wgn != 2 || c.pipe != 3 || c.bstage)
-    return c;
-  if (r.ffn || r.out_pre || r.batch != 1 || !a_kcontig(r.layout) || !b_kcontig(r.layout) ||
-      r.K < 2 * mmk::kSlabK || (int64_t)256 * r.K * 2 >= (int64_t(1) << 31))
-    return c;
-  constexpr int64_t kGrid = 256;
-  const int64_t passes256 = cdiv(cdiv(r.M, 256) * cdiv(r.N, 256), kGrid);
-  const int64_t passes192 = cdiv(cdiv(r.M, 256) * cdiv(r.N, 192), kGrid);
-  if (passes192 * 78 < passes256 * 100) c.bn = 192;
+  if (c.forced || c.wgm != 2 || c.wgn != 2 || c.pipe != 3 || c.bstage) return c;
+  if (!((c.bm == 256 && c.bn == 256) || (c.bm == 128 && c.bn == 128)) || !narrow_eligible(r)) return c;
+  switch (best_unsplit_kind(r, nullptr)) {
+    case kTile256: c.bm = 256; c.bn = 256; break;
+    case kTile192: c.bm = 256; c.bn = 192; break;
+    case kTile128: c.bm = 256; c.bn = 128; break;
+    default: c.bm = 128; c.bn = 128; break;
+  }
   return c;
 }
 

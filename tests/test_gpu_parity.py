@@ -47,6 +47,9 @@ CONFIGS = [
     # and forms fall back to 256 x 256), also on a small grid
     "BM=256,BN=192,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3",
     "BM=256,BN=192,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
+    # 256 x 128 slab tiles (the same restriction), also on a small grid
+    "BM=256,BN=128,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3",
+    "BM=256,BN=128,WM=2,WN=2,G=2,XCD=0,KALT=1,GRID=3,PIPE=3",
     # 64 x 64 tiles: K <= 256 runs the kernel holding all of K in LDS (here
     # on a small grid, several tiles per workgroup); PIPE=0 keeps the basic
     # two-stage kernel at every K
@@ -350,8 +353,9 @@ def test_preact_random_matches_single_output(dev, epi):
     assert torch.equal(pre.view(torch.int16), pre_one.view(torch.int16))
 
 
-# (M, N, K, config): automatic chunk-major (16 chunks per tile, one per
-# workgroup); forced stream-K on 140 tiles (ranges of 3/4 of a tile);
+# (M, N, K, config): automatic chunk-major (the cost model's chunk count and
+# tile width, one chunk per workgroup); forced stream-K on 140 tiles (ranges
+# of 3/4 of a tile);
 # ranges of two chunks of three that cross tile boundaries; ranges of
 # three of four; uneven chunk-major chunks (64 super-steps in 7); and K not a
 # multiple of 64 (the last chunk of each tile ends with a partial super-step),

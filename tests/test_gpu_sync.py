@@ -172,17 +172,18 @@ def test_linear_bias_staged(libs, grid):
             binding.LAYOUTS["nt"], binding.EPILOGUES[epi], stream()), "mm_linear"), [out]))
 
 
+@pytest.mark.parametrize("bn", [192, 128])
 @pytest.mark.parametrize("grid", [0, 5])
-def test_linear_narrow_tiles(libs, grid):
-    """The 256 x 192 instance of the slab kernel (ragged tiles; on a grid of
-    5 the ring runs on across several tiles per workgroup)."""
+def test_linear_narrow_tiles(libs, bn, grid):
+    """The 256 x 192 and 256 x 128 instances of the slab kernel (ragged tiles;
+    on a grid of 5 the ring runs on across several tiles per workgroup)."""
     dev = torch.device("cuda:0")
     M, N, K = 1040, 776, 1024
-    cfg = f"BM=256,BN=192,WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
+    cfg = f"BM=256,BN={bn},WM=2,WN=2,G=4,XCD=1,KALT=1,PIPE=3,GRID={grid}"
     A, B = operands(M, N, K, "nt", 990 + grid, dev)
     bias = synth.randn_bf16((N,), 1.0, 995).to(dev)
     assert_slab(libs, cfg, "linear", M, N, K, "nt")
-    say("linear, 256 x 192 tiles", (M, N, K), cfg)
+    say("linear, narrow tiles", (M, N, K), cfg)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_linear(
         A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
@@ -193,7 +194,8 @@ def test_linear_narrow_tiles(libs, grid):
         "mm_matmul"), [out32]))
 
 
-@pytest.mark.parametrize("layout,bn", [("nt", 256), ("nt", 192), ("nn", 256), ("tn", 256), ("tt", 256)])
+@pytest.mark.parametrize("layout,bn", [("nt", 256), ("nt", 192), ("nt", 128), ("nn", 256), ("tn", 256),
+                                       ("tt", 256)])
 @pytest.mark.parametrize("grid", [0, 5])
 def test_ragged_k(libs, layout, bn, grid):
     """The instances whose last super-step per tile is a partial one (K = 1000:

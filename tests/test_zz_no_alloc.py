@@ -47,8 +47,8 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 
 
 # (M, N, K, layout): two calls in a row, the second smaller, both split by the
-# automatic rule (20 tiles of 256 x 192 in 8 chunks: 160 slots = 40 MiB of
-# scratch; then 9 tiles in 4 chunks: 36 slots); then a stored-[K][N] product
+# automatic rule (32 tiles of 256 x 128 in 8 chunks: 256 slots, the whole
+# 64 MiB of scratch; then 12 tiles in 10 chunks: 120 slots); then a stored-[K][N] product
 # (256 x 256 tiles), a shape that runs unsplit, and one whose K is not a
 # multiple of 64 (never split: the slab kernel's ragged instance)
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
