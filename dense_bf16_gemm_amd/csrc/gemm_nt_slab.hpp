@@ -124,6 +124,47 @@ __device__ __forceinline__ void spread_first_row_a() {
   __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 }
+// Rows of 4 MFMAs leave too few slots for a k-step head in one row.  With
+// them the first k-step's head spans rows 0..2 (12 MFMAs: the scalar chain
+// over the first eight, then the three copies and six fragment reads) and
+// the second k-step's its first two rows (8 MFMAs: the weight descriptors
+// over the first three, then three copies and five fragment reads).
+__device__ __forceinline__ void spread_first_rows_a4() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x006, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+__device__ __forceinline__ void spread_rows_b4() {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+}
 template <int MPR>
 __device__ __forceinline__ void spread_first_row_b() {
   if constexpr (MPR == 4) {
@@ -611,6 +652,8 @@ gemm_nt_slab(GemmParams p) {
 #endif
 
     // k-step 2q: MFMAs on half 0; half 1 of q (same units) into fa and fb[1]
+    // (the first kHeadRows rows form the head's scheduling region)
+    constexpr int kHeadRows = FN == 4 ? 3 : 1;
 #pragma unroll
     for (int r = 0; r < FM; ++r) {
       mfma_half(r, 0, 0);
@@ -619,16 +662,20 @@ gemm_nt_slab(GemmParams p) {
         read_b(1, 2 * r, 1, b_cur);
         read_b(1, 2 * r + 1, 1, b_cur);
       }
-      if (r == 0) {
+      const bool head = r < kHeadRows, head_end = r == kHeadRows - 1;
+      if (head) {
         mfma_half(r, 0, 1);
-        spread_first_row_a<FN>();
+        if (head_end) {
+          if constexpr (FN == 4) spread_first_rows_a4();
+          else spread_first_row_a<FN>();
+        }
       } else {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(r, 0, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (!head || head_end) __builtin_amdgcn_sched_barrier(0);
       read_a(r, 1, a_cur);
-      __builtin_amdgcn_sched_barrier(0);
+      if (!head || head_end) __builtin_amdgcn_sched_barrier(0);
     }
 
     // k-step 2q+1, first row (4): its fragments are already in registers
@@ -648,7 +695,8 @@ gemm_nt_slab(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     read_a(4, 0, a_nxt);
     // rows 5, 6, 7, 0, 1, 2, 3: half 0 of q+1 into fa and fb[0]; the weight
-    // slab of q+2
+    // slab of q+2 (rows p = 1 .. kHeadRowsB form the head's region)
+    constexpr int kHeadRowsB = FN == 4 ? 2 : 1;
 #pragma unroll
     for (int p = 1; p < FM; ++p) {
       const int r = (p + 4) & 7;
@@ -661,9 +709,13 @@ gemm_nt_slab(GemmParams p) {
         read_b(0, 2 * (p - 1), 0, b_nxt);
         read_b(0, 2 * (p - 1) + 1, 0, b_nxt);
       }
-      if (p == 1) {
+      const bool head = p <= kHeadRowsB, head_end = p == kHeadRowsB;
+      if (head) {
         mfma_half(r, 1, 1);
-        spread_first_row_b<FN>();
+        if (head_end) {
+          if constexpr (FN == 4) spread_rows_b4();
+          else spread_first_row_b<FN>();
+        }
       } else {
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(r, 1, 1);
@@ -673,10 +725,12 @@ gemm_nt_slab(GemmParams p) {
         // carried unit) goes between its MFMAs instead of after them
         read_a(r, 0, a_nxt);
         spread_loop_latch<FN>();
-      } else {
+      } else if (!head || head_end) {
         __builtin_amdgcn_sched_barrier(0);
         read_a(r, 0, a_nxt);
         __builtin_amdgcn_sched_barrier(0);
+      } else {
+        read_a(r, 0, a_nxt);
       }
     }
     cur_unit = nua;
