@@ -165,6 +165,58 @@ __device__ __forceinline__ void spread_rows_b4() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
 }
+// Rows of 8 MFMAs: the first k-step's head spans two rows (16 MFMAs).
+__device__ __forceinline__ void spread_first_rows_a8() {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+// Rows of 6 MFMAs: both heads span two rows (12 MFMAs).
+__device__ __forceinline__ void spread_first_rows_a6() {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+__device__ __forceinline__ void spread_rows_b6() {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+  }
+}
 template <int MPR>
 __device__ __forceinline__ void spread_first_row_b() {
   if constexpr (MPR == 4) {
@@ -653,7 +705,7 @@ gemm_nt_slab(GemmParams p) {
 
     // k-step 2q: MFMAs on half 0; half 1 of q (same units) into fa and fb[1]
     // (the first kHeadRows rows form the head's scheduling region)
-    constexpr int kHeadRows = FN == 4 ? 3 : 1;
+    constexpr int kHeadRows = FN == 4 ? 3 : 2;
 #pragma unroll
     for (int r = 0; r < FM; ++r) {
       mfma_half(r, 0, 0);
@@ -667,7 +719,8 @@ gemm_nt_slab(GemmParams p) {
         mfma_half(r, 0, 1);
         if (head_end) {
           if constexpr (FN == 4) spread_first_rows_a4();
-          else spread_first_row_a<FN>();
+          else if constexpr (FN == 6) spread_first_rows_a6();
+          else spread_first_rows_a8();
         }
       } else {
         __builtin_amdgcn_sched_barrier(0);
@@ -696,7 +749,7 @@ gemm_nt_slab(GemmParams p) {
     read_a(4, 0, a_nxt);
     // rows 5, 6, 7, 0, 1, 2, 3: half 0 of q+1 into fa and fb[0]; the weight
     // slab of q+2 (rows p = 1 .. kHeadRowsB form the head's region)
-    constexpr int kHeadRowsB = FN == 4 ? 2 : 1;
+    constexpr int kHeadRowsB = FN == 4 || FN == 6 ? 2 : 1;
 #pragma unroll
     for (int p = 1; p < FM; ++p) {
       const int r = (p + 4) & 7;
@@ -714,6 +767,7 @@ gemm_nt_slab(GemmParams p) {
         mfma_half(r, 1, 1);
         if (head_end) {
           if constexpr (FN == 4) spread_rows_b4();
+          else if constexpr (FN == 6) spread_rows_b6();
           else spread_first_row_b<FN>();
         }
       } else {
