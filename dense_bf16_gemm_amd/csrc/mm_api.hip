@@ -27,6 +27,7 @@
 #include "gemm_pp.hpp"
 #include "gemm_nt_slab.hpp"
 #include "gemm_small.hpp"
+#include "gemm_skinny.hpp"
 
 // Split-K partial tiles of mm_matmul_noalloc: a fixed device array instead of
 // a caller's workspace, for callers that cannot allocate.  64 MiB = one
@@ -897,12 +898,85 @@ mm_status run_empty_k(const Request& r, void* stream) {
   return MM_OK;
 }
 
+// ----------------------------------------------------------------------------
+// Skinny products (gemm_skinny): K-contiguous single-weight single-output
+// products of at most 16 rows against at least 8 MiB of weights, unless a
+// configuration is forced.  Without a workspace each 16-column block is one
+// workgroup; with one, K is also cut into S slices (at least 512 k each, at
+// most 16) so that about 1024 workgroups stream the weights.
+// ----------------------------------------------------------------------------
+constexpr int64_t kSkinnyTargetWgs = 1024;
+
+bool skinny_shape(const Request& r) {
+  return a_kcontig(r.layout) && b_kcontig(r.layout) && !r.ffn && !r.out_pre && r.batch == 1 &&
+         r.M <= mmk::kSkinnyMaxM && r.K >= 256 && r.N * r.K >= (int64_t(1) << 22);
+}
+
+struct SkinnyPlan {
+  int kc = 0;       // k per slice
+  int slices = 1;   // S
+};
+
+SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
+  SkinnyPlan sp;
+  int64_t S = 1;
+  if (max_slices > 1) {
+    S = cdiv(kSkinnyTargetWgs, cdiv(r.N, 16));
+    S = std::min<int64_t>({S, r.K / 512, 16, max_slices});
+    if (S < 1) S = 1;
+  }
+  sp.kc = (int)(cdiv(cdiv(r.K, S), 32) * 32);
+  sp.slices = (int)cdiv(r.K, sp.kc);
+  return sp;
+}
+
+int64_t skinny_ws_bytes(const Request& r, const SkinnyPlan& sp) {
+  return sp.slices > 1 ? (int64_t)sp.slices * r.M * r.N * 4 : 0;
+}
+
+mm_status run_skinny(const Request& r, void* stream) {
+  // with the static scratch, as many slices as it holds
+  const int64_t per_slice = r.M * r.N * 4;
+  SkinnyPlan sp = skinny_plan(r, r.ws ? (r.static_ws ? r.ws_bytes / per_slice : 16) : 1);
+  const int64_t need = skinny_ws_bytes(r, sp);
+  if (need > 0) {
+    if (r.ws_bytes < need) return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
+    if (!aligned(r.ws, 256)) return fail(MM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  }
+  mmk::SkinnyParams p;
+  p.A = static_cast<const uint16_t*>(r.A);
+  p.B = static_cast<const uint16_t*>(r.B);
+  p.bias = static_cast<const uint16_t*>(r.bias);
+  p.out = r.out;
+  p.part = need > 0 ? static_cast<float*>(r.ws) : nullptr;
+  p.M = (int)r.M;
+  p.N = (int)r.N;
+  p.K = (int)r.K;
+  p.kc = sp.kc;
+  p.slices = sp.slices;
+  p.epi = r.epi;
+  p.out_f32 = r.out_f32 ? 1 : 0;
+  const int64_t grid = cdiv(r.N, 16) * sp.slices;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::gemm_skinny), dim3((unsigned)grid), dim3(256),
+                                 args, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny): ") + hipGetErrorString(e));
+  if (sp.slices > 1) {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::skinny_reduce), dim3((unsigned)cdiv(r.M * r.N, 256)),
+                        dim3(256), args, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny reduction): ") + hipGetErrorString(e));
+  }
+  return MM_OK;
+}
+
 mm_status run(const Request& r, void* stream) {
   mm_status s = validate(r);
   if (s != MM_OK) return s;
   if (r.M == 0 || r.N == 0) return MM_OK;
   if (r.K == 0) return run_empty_k(r, stream);
   const Config c = choose_config_for(r);
+  if (!c.forced && skinny_shape(r)) return run_skinny(r, stream);
   Plan pl;
   SkPlan sp;
   s = plan_host(r, c, &pl);
@@ -1057,9 +1131,13 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
   *bytes = 0;
   Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
             false, form == 1};
-  if (M == 0 || N == 0 || K == 0 || !splitk_shape(r)) return MM_OK;
+  if (M == 0 || N == 0 || K == 0) return MM_OK;
   const Config c = choose_config_for(r);
-  if (c.sk == 1) return MM_OK;
+  if (!c.forced && skinny_shape(r)) {
+    *bytes = skinny_ws_bytes(r, skinny_plan(r, 16));
+    return MM_OK;
+  }
+  if (!splitk_shape(r) || c.sk == 1) return MM_OK;
   int cus = 0, occ = 0;
   mm_status s;
   if ((s = device_cus(&cus)) != MM_OK) return s;
@@ -1166,7 +1244,13 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
   // a plain product that a workspace would split: chunks per tile and tile
   // width on the current device (queries the device; left out without one)
   char split[32] = "";
-  if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
+  const bool skinny = M > 0 && N > 0 && K > 0 && !c.forced && skinny_shape(rq);
+  if (skinny) {
+    // the skinny kernel (no device query): S slices of K with a workspace
+    kernel = "gemm_skinny";
+    const SkinnyPlan sp = skinny_plan(rq, 16);
+    if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx16,", sp.slices);
+  } else if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
               false, false};
     int cus = 0, occ = 0;

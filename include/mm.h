@@ -155,14 +155,17 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * notes: splitting the K loop over workgroups, split-K and stream-K, named
  * there and left out of the persistent scheduler).  When a single-weight
  * product -- mm_matmul, or mm_linear with any epilogue, any layout, K >= 128
- * -- has fewer 256 x 256 (or 256 x 192) output tiles than the GPU has
- * resident workgroups (at most half as many) and K long enough that each
- * chunk spans at least 32 x 64 of it, the _ws entry points below cut each
- * tile's K loop into chunks and deal the chunks of all tiles to the resident
- * workgroups (one chunk each, or equal contiguous ranges: stream-K); each
- * piece leaves its fp32 partial tile in this workspace (one 256 KiB slot per
- * workgroup, two per stream-K workgroup), and a second kernel on the same
- * stream adds them in k order and applies the epilogue once.
+ * -- has fewer 256 x 256 (256 x 192, 256 x 128) output tiles than the GPU
+ * has resident workgroups (at most half as many) and a cost model of the
+ * kernels finds a split faster than the best unsplit run (chunks of at least
+ * 8 x 64 of K), the _ws entry points below cut each tile's K loop into chunks
+ * and deal the chunks of all tiles to the resident workgroups (one chunk
+ * each, or equal contiguous ranges: stream-K); each piece leaves its fp32
+ * partial tile in this workspace (one 256 KiB slot per workgroup, two per
+ * stream-K workgroup), and a second kernel on the same stream adds them in k
+ * order and applies the epilogue once.  Products of at most 16 rows (the
+ * skinny kernel, see mm_describe_config) use it for fp32 partial outputs of
+ * S slices of K (S x M x N x 4 bytes), added in k order the same way.
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
  *   bytes   receives the size a call of this shape on the current device may
  *           use; 0 = the shape runs without one.  Queries the device (CU
@@ -248,7 +251,10 @@ mm_status mm_set_config(const char* spec);
  * and is left out when there is none); and last KERNEL=<family>.  The tile
  * and KERNEL parts describe a call without a workspace; with SPLIT present,
  * a call given a workspace (mm_matmul_ws, mm_linear_ws, mm_matmul_noalloc)
- * runs the slab kernel on 256 x <tile width> tiles instead.  K = 0 names
+ * runs the slab kernel on 256 x <tile width> tiles instead.  Products of at
+ * most 16 rows against at least 8 MiB of weights (layout MM_NT, one weight,
+ * no forced configuration) name gemm_skinny, with SPLIT=<k slices>x16 when a
+ * workspace would cut K (no device query).  K = 0 names
  * empty_k_fill.  form: 0 matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE
  * for bad args. */
 mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,

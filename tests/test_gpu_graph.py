@@ -9,8 +9,9 @@ synchronizes), and every replay is checked, not just the first.  The cases
 cover the slab kernel with a fused epilogue, the horizontally fused FFN, and
 split-K with its two launches, through a caller's workspace and through the
 library's static scratch, a split linear form whose reduction applies
-the epilogue, and a K that is not a multiple of 64 (the slab kernel's
-ragged instance).
+the epilogue, a K that is not a multiple of 64 (the slab kernel's
+ragged instance), and a skinny product (16 rows, K in slices, with its
+reduction).
 """
 
 import pytest
@@ -73,7 +74,13 @@ def test_graph_replays_equal_eager_calls(dev):
     Wr = synth.randn_bf16((Nr, Kr), Kr ** -0.5, 811).to(dev)
     br = synth.randn_bf16((Nr,), 1.0, 812).to(dev)
     y6 = torch.empty((Mr, Nr), dtype=torch.bfloat16, device=dev)
-    outs = (y1, y2, y3, y4, y5, y6)
+    Mk, Nk, Kk = 16, 8192, 4096
+    assert binding.describe_config("linear", Mk, Nk, Kk).endswith("KERNEL=gemm_skinny")
+    xk = synth.randn_bf16((Mk, Kk), 1.0, 813).to(dev)
+    Wk = synth.randn_bf16((Nk, Kk), Kk ** -0.5, 814).to(dev)
+    wsk = torch.empty(max(binding.workspace_size("linear", Mk, Nk, Kk), 1), dtype=torch.uint8, device=dev)
+    y7 = torch.empty((Mk, Nk), dtype=torch.bfloat16, device=dev)
+    outs = (y1, y2, y3, y4, y5, y6, y7)
 
     def calls():
         mm.linear(x, W, bias, "bias_gelu_tanh", out=y1)
@@ -82,6 +89,7 @@ def test_graph_replays_equal_eager_calls(dev):
         noalloc(As, Bs, Ms, Ns, Ks, y4)
         mm.linear(As, Bs, bias_s, "bias_gelu_tanh", out=y5, workspace=ws)
         mm.linear(xr, Wr, br, "bias_gelu_tanh", out=y6)
+        mm.linear(xk, Wk, None, "gelu_tanh", out=y7, workspace=wsk)
 
     calls()
     torch.cuda.synchronize()

@@ -937,6 +937,68 @@ def test_batched_ragged_k_slab(dev, layout):
         np.testing.assert_array_equal(out[b].cpu().numpy(), ref)
 
 
+# ------------------------------------------------------------ skinny products
+# (M, N, K): at most 16 activation rows against at least 8 MiB of weights --
+# ragged N and K (multiples of 8), slices of K that end mid-step, one row
+SKINNY_SHAPES = [(1, 4096, 1024), (7, 1000, 8200), (16, 8192, 1032), (9, 4104, 4096), (16, 2048, 2056),
+                 (13, 3000, 4096), (2, 1032, 8192)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_SHAPES)
+@pytest.mark.parametrize("ws", [False, True])
+def test_skinny_mapping_bitexact(dev, shape, ws):
+    """The skinny kernel, unsplit (no workspace) and with K cut into slices
+    (a workspace): bf16 with a bias from integer operands, and fp32 from
+    dense integers, against the oracle's bits; guard bands checked."""
+    M, N, K = shape
+    cfg = binding.describe_config("linear", M, N, K)
+    say("skinny", shape, "ws" if ws else "no ws", cfg)
+    assert cfg.endswith("KERNEL=gemm_skinny"), cfg
+    nbytes = binding.workspace_size("linear", M, N, K) if ws else 0
+    wsp = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=dev)
+    lib = binding.load()
+    ops = synth.mapping_operands(M, N, K, "nt", seed=M + 3 * N + K, with_bias=True)
+    A, B, bias = ops["A"].to(dev), ops["B"].to(dev), ops["bias"].to(dev)
+    buf, out = guarded_out(M, N, False, dev)
+    st = lib.mm_linear_ws(A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K,
+                          binding.LAYOUTS["nt"], binding.EPILOGUES["bias"], wsp.data_ptr() if ws else None,
+                          nbytes, stream())
+    binding.check(st, "mm_linear_ws")
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    _, bits = oracle.gemm(synth.bits(ops["A"]), synth.bits(ops["B"]), "nt", "bias", bias=synth.bits(ops["bias"]))
+    np.testing.assert_array_equal(to_bits(out), bits)
+    del buf, out
+    Ad, Bd = synth.dense_int_operands(M, N, K, "nt", seed=M + N)
+    buf, out = guarded_out(M, N, True, dev)
+    st = lib.mm_matmul_ws(Ad.to(dev).data_ptr(), Bd.to(dev).data_ptr(), out.data_ptr(), M, N, K,
+                          binding.LAYOUTS["nt"], 1, wsp.data_ptr() if ws else None, nbytes, stream())
+    binding.check(st, "mm_matmul_ws")
+    torch.cuda.synchronize()
+    assert guards_intact(buf, M, N)
+    ref, _ = oracle.gemm(synth.bits(Ad), synth.bits(Bd), "nt")
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("shape", [(16, 8192, 8192), (5, 4096, 4104)])
+@pytest.mark.parametrize("epi", ["bias_gelu_tanh", "gelu_tanh", "none"])
+def test_skinny_random(dev, shape, epi):
+    """Random operands through mm.linear (its automatic workspace: K in
+    slices) within the bf16 tolerance; run to run identical."""
+    M, N, K = shape
+    say("skinny random", shape, epi)
+    x = synth.randn_bf16((M, K), 1.0, 91)
+    W = synth.randn_bf16((N, K), K ** -0.5, 92)
+    b = synth.randn_bf16((N,), 1.0, 93)
+    bd = b.to(dev) if "bias" in epi else None
+    o1 = mm.linear(x.to(dev), W.to(dev), bd, epi)
+    o2 = mm.linear(x.to(dev), W.to(dev), bd, epi)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    y, _ = oracle.gemm(synth.bits(x), synth.bits(W), "nt", epi, bias=synth.bits(b) if bd is not None else None)
+    assert tol_excess(o1.float().cpu().numpy(), y, 2e-2) <= 0
+
+
 # ------------------------------------------------------------ non-finite inputs
 def nonfinite_case(M, N, K, layout, seed):
     """op(A) [M,K], op(B) [K,N] (bf16, N(0,1)-like) with +-inf and NaN entries

@@ -49,10 +49,11 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 # (M, N, K, layout): two calls in a row, the second smaller, both split by the
 # automatic rule (32 tiles of 256 x 128 in 8 chunks: 256 slots, the whole
 # 64 MiB of scratch; then 12 tiles in 10 chunks: 120 slots); then a stored-[K][N] product
-# (256 x 256 tiles), a shape that runs unsplit, and one whose K is not a
-# multiple of 64 (never split: the slab kernel's ragged instance)
+# (256 x 256 tiles), a shape that runs unsplit, one whose K is not a
+# multiple of 64 (never split: the slab kernel's ragged instance), and a
+# skinny product (16 rows: its fp32 partial outputs of 2 slices of K)
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
-            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt")]
+            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt"), (16, 8192, 4096, "nt")]
 UNSPLIT = {(520, 392, 512), (2900, 3000, 1032)}
 
 
