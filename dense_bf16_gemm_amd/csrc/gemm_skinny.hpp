@@ -4,27 +4,34 @@
 //
 // Such a product is bound by reading W once from HBM; its MFMA work is small.
 // The 256-row tiles of the slab kernel would spend almost all of their MFMAs
-// on rows past M, so here a workgroup takes 16 of W's rows (16 output
-// columns) and streams them once: its four waves split the k range into four
-// parts, each wave loads its weight and activation fragments straight from
-// global memory into registers, a few 32-k steps ahead, and the parts meet in
-// LDS in a fixed order.  With a workspace the k range is also split over S
-// workgroups per column block: each writes its fp32 sums to slice s of the
-// workspace and skinny_reduce adds the slices in k order.  Results: fp32 sums
-// of the bf16 products, the epilogue on the sum, one rounding -- the
-// contraction and epilogue of the other kernels.
+// on rows past M, so here a workgroup takes 64 of W's rows (64 output
+// columns) and streams them once through a ring of three LDS stages of 256
+// k.  Each wave-wide copy fills two rows' 512-byte runs straight from
+// memory into LDS (buffer loads to LDS: no registers), the 16 activation
+// rows of the stage come the same way, and the four waves each multiply a
+// quarter of the stage's k-steps with MFMAs whose fragments are read from
+// LDS; the waves' parts meet in LDS in a fixed order at the end.  With a
+// workspace K may also be cut into S slices (when that fills the CUs
+// better): each writes its fp32 sums to slice s of the workspace and
+// skinny_reduce adds the slices in k order.  Results: fp32 sums of the bf16
+// products, the epilogue on the sum, one rounding -- the contraction and
+// epilogue of the other kernels.
 //
-// Measured against the slab kernel's split path (256 x 128 tiles, rows past
-// M computed and dropped), with a workspace: 16 x 14336 x 4096 35.6 -> 30.0
-// us, 16 x 8192 x 8192 34.2 -> 33.4 us, 8 x 8192 x 8192 34.2 -> 28.3 us.  A
-// 64-row form of the same design (four waves each re-reading the activation
-// fragments for their own column block) was slower than the slab path (80
-// against 35 us at 64 x 8192 x 8192), and non-temporal weight loads cost a
-// third (each load reads 64-byte halves of 16 lines; the other halves then
-// miss).
+// Whole-row runs matter: with fragments loaded straight into registers
+// (each load reading 64 bytes of 16 rows) the same products ran at 3.0-3.3
+// TB/s of weights; a streaming probe reading whole 1 KiB runs per load
+// reached 5.1 TB/s.  Measured with the weights rotated over more than 1 GiB
+// of copies (no cache reuse), in us against the register-fragment form and
+// the platform BLAS: 16 x 28672 x 8192 144 -> 100 (116), 16 x 14336 x 4096
+// 40 -> 28.2 (29.0), 16 x 4096 x 14336 41 -> 25.5 (25.8), 16 x 8192 x 8192
+// 43 -> 32.9 (28.8).  Not kept: 32-row groups with 512-k stages (one row per
+// copy; 33-35 us at 8192 x 8192, 115 us at 28672 x 8192), 48-row groups,
+// four or five stages (no gain), and rotating each workgroup's first stage
+// (faster at 14336 x 4096, 6 us slower at 8192 x 8192).
 #pragma once
 
 #include "gemm_kernel.hpp"
+#include "gemm_nt_pipe.hpp"
 
 namespace mmk {
 
@@ -42,7 +49,23 @@ struct SkinnyParams {
 };
 
 constexpr int kSkinnyMaxM = 16;
-constexpr int kSkinnyDepth = 4;  // 32-k steps of loads in flight per wave
+constexpr int kSkinnyRows = 64;    // weight rows (output columns) per workgroup
+constexpr int kSkinnyKD = 256;     // k per stage: 512-byte runs, two rows per copy
+constexpr int kSkinnyStages = 3;   // ring of stages in LDS (120 KiB)
+constexpr int kSkinnyStageBytes = (kSkinnyRows + kSkinnyMaxM) * kSkinnyKD * 2;
+
+// s_waitcnt for the copies of `ahead` stages (at most A) left in flight
+template <int PER, int A>
+__device__ __forceinline__ void skinny_wait(int ahead) {
+  if constexpr (A == 0) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  } else {
+    if (ahead >= A)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(A * PER));
+    else
+      skinny_wait<PER, A - 1>(ahead);
+  }
+}
 
 // epilogue of one output: + bias, activation, one rounding
 __device__ __forceinline__ void skinny_store(const SkinnyParams& p, int m, int n, float v) {
@@ -55,70 +78,150 @@ __device__ __forceinline__ void skinny_store(const SkinnyParams& p, int m, int n
 }
 
 __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
-  constexpr int D = kSkinnyDepth;
-  __shared__ f32x4 red[3 * 64];
+  constexpr int R = kSkinnyRows, KD = kSkinnyKD, NS = kSkinnyStages, SB = kSkinnyStageBytes;
+  constexpr int P = KD * 2;             // bytes of a row in a stage
+  constexpr int CPR = KD / 8;           // 16-byte chunks of a row in a stage
+  constexpr int RPI = 64 / CPR;         // rows per wave-wide copy
+  constexpr int WC = R / RPI / 4, XC = kSkinnyMaxM / RPI / 4;  // copies per wave and stage
+  static_assert(CPR >= 16 && CPR <= 64 && R % (4 * RPI) == 0 && kSkinnyMaxM % (4 * RPI) == 0, "stage shape");
+  constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+  constexpr uint32_t kOob = 0x80000000u;  // past every record count below
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SB];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the k part
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lx = lane & 15, lk = lane >> 4;
-  const int nblocks = (p.N + 15) / 16;
-  const int s = __builtin_amdgcn_readfirstlane((int)blockIdx.x / nblocks);
-  const int nb = (int)blockIdx.x - s * nblocks;
+  const int ngroups = (p.N + R - 1) / R;
+  const int s = __builtin_amdgcn_readfirstlane((int)blockIdx.x / ngroups);
+  const int g = __builtin_amdgcn_readfirstlane((int)blockIdx.x - s * ngroups);
   const int M = p.M, N = p.N, K = p.K;
+  const int64_t n0 = (int64_t)g * R;
 
-  // the workgroup's slice [kbeg, kend) of K, cut into four parts of whole
-  // 32-k steps, one per wave
+  // the workgroup's slice [kbeg, kend) of K in stages of KD
   const int kbeg = s * p.kc;
   const int kend = min(K, kbeg + p.kc);
-  const int steps = (kend - kbeg + 31) / 32;
-  const int per = (steps + 3) / 4;
-  const int j0 = wave * per, j1 = min(steps, j0 + per);
-  const int n = nb * 16 + lx;  // the weight row (output column) this lane loads
-  const bool n_ok = n < N, m_ok = lx < M;
-  const uint16_t* wrow = p.B + (int64_t)(n_ok ? n : 0) * K;
-  const uint16_t* xrow = p.A + (int64_t)(m_ok ? lx : 0) * K;
+  const int nst = (kend - kbeg + KD - 1) / KD;
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 wq[D], xq[D];
-  // fragments of step j: weight row n and activation row lx, 8 k from
-  // kbeg + 32 j + 8 lk; zeros past the part, K, N or M (masked lanes keep an
-  // address inside the operands: k = 0 of row 0)
-  auto load = [&](int j, int slot) __attribute__((always_inline)) {
-    const int k = kbeg + 32 * j + 8 * lk;
-    const bool k_ok = j < j1 && k < kend;
-    const int kk = k_ok ? k : 0;
-    wq[slot] = (k_ok && n_ok) ? *reinterpret_cast<const u32x4*>(wrow + kk) : zero4();
-    xq[slot] = (k_ok && m_ok) ? *reinterpret_cast<const u32x4*>(xrow + kk) : zero4();
+  // Copies: a stage holds KD k of the group's R weight rows and of the 16
+  // activation rows; each wave-wide LDS copy fills RPI rows of it.  The
+  // lane that fills chunk position c of row r fetches the row's 16-byte
+  // chunk c ^ (r & 15), so that the fragment reads of 16 rows at one chunk
+  // fall in 16 distinct bank groups.  Rows past N or M lie past the
+  // descriptors' record counts and read as zeros; chunks past the slice's
+  // end are pushed past them.
+  const uint64_t rec_w64 = (uint64_t)(N - n0) * (uint64_t)K * 2u;
+  const uint32_t rec_w = rec_w64 > 0x7fffffffull ? 0x7fffffffu : (uint32_t)rec_w64;
+  const uint32_t rec_x = (uint32_t)M * (uint32_t)K * 2u;
+  uint32_t voff_w[WC], voff_x[XC];
+  int chunk_w[WC], chunk_x[XC];
+#pragma unroll
+  for (int i = 0; i < WC; ++i) {
+    const int r = (wave * WC + i) * RPI + lane / CPR;
+    chunk_w[i] = (lane % CPR) ^ (r & 15);
+    voff_w[i] = (uint32_t)r * (uint32_t)K * 2u + 16u * (uint32_t)chunk_w[i];
+  }
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int r = (wave * XC + i) * RPI + lane / CPR;
+    chunk_x[i] = (lane % CPR) ^ (r & 15);
+    voff_x[i] = (uint32_t)r * (uint32_t)K * 2u + 16u * (uint32_t)chunk_x[i];
+  }
+  auto rsrc = [&](const uint16_t* base, uint32_t rec) __attribute__((always_inline)) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* ptr = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ptr, (short)0, (int)__builtin_amdgcn_readfirstlane(rec), kRsrcWord3);
   };
+  auto copy_stage = [&](int st) __attribute__((always_inline)) {
+    char* slot = smem + (st % NS) * SB;
+    const int k0 = kbeg + st * KD;
+    const int lim = kend - k0;  // k of the stage inside the slice
+    // the descriptors start at k0: the record counts shrink by as much
+    const __amdgpu_buffer_rsrc_t rw = rsrc(p.B + n0 * K + k0, rec_w - 2u * (uint32_t)k0);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(p.A + k0, rec_x - 2u * (uint32_t)k0);
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(j0 + d, d);
-  for (int j = j0; j < j1; j += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xq[d]), __builtin_bit_cast(bf16x8, wq[d]),
-                                                    acc, 0, 0, 0);
-      load(j + d + D, d);
+    for (int i = 0; i < WC; ++i) {
+      const uint32_t off = voff_w[i] | (lim < KD && 8 * chunk_w[i] >= lim ? kOob : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(slot + (wave * WC + i) * 1024), 16, off, 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const uint32_t off = voff_x[i] | (lim < KD && 8 * chunk_x[i] >= lim ? kOob : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(slot + R * P + (wave * XC + i) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  // wave w multiplies k-steps w*KS .. w*KS+KS-1 (32 k each) of every stage
+  constexpr int KS = KD / 128;
+  f32x4 acc[R / 16];
+#pragma unroll
+  for (int c = 0; c < R / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const char* slot = smem + (st % NS) * SB;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const int pos = ((4 * (KS * wave + q) + lk) ^ lx) * 16;
+      const u32x4 xf = *reinterpret_cast<const u32x4*>(slot + (R + lx) * P + pos);
+#pragma unroll
+      for (int c = 0; c < R / 16; ++c) {
+        const u32x4 wf = *reinterpret_cast<const u32x4*>(slot + (16 * c + lx) * P + pos);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf),
+                                                         __builtin_bit_cast(bf16x8, wf), acc[c], 0, 0, 0);
+      }
+    }
+  };
+
+  // ring of NS stages: stage st+NS-1 is fetched into the slot that stage
+  // st-1 held, once every wave is past it
+  constexpr int kCopies = WC + XC;  // per wave and stage
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nst) copy_stage(i);
+  for (int st = 0; st < nst; ++st) {
+    // stage st's copies are done when at most those of the stages after it
+    // remain (a plain barrier: a fence here would wait for every copy)
+    skinny_wait<kCopies, NS - 2>(min(NS - 2, nst - 1 - st));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nst) copy_stage(st + NS - 1);
+    compute(st);
   }
 
-  // the k parts meet in LDS: parts 1..3 store, part 0 adds them in order
-  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+  // the waves' k parts meet in LDS: waves 1..3 store, wave 0 adds in order
   __syncthreads();
-  if (wave > 0 || !n_ok) return;
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  if (wave > 0) {
+#pragma unroll
+    for (int c = 0; c < R / 16; ++c) red[((wave - 1) * (R / 16) + c) * 64 + lane] = acc[c];
+  }
+  __syncthreads();
+  if (wave > 0) return;
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
-    const f32x4 v = red[q * 64 + lane];
-    acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
-  }
-  // lane (lx, lk) holds rows 4 lk + i, i = 0..3, of column n
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * lk + i;
-    if (m >= M) continue;
-    if (p.slices > 1)
-      p.part[((int64_t)s * M + m) * N + n] = acc[i];
-    else
-      skinny_store(p, m, n, acc[i]);
+    for (int c = 0; c < R / 16; ++c) {
+      const f32x4 v = red[(q * (R / 16) + c) * 64 + lane];
+      acc[c] = f32x4{acc[c][0] + v[0], acc[c][1] + v[1], acc[c][2] + v[2], acc[c][3] + v[3]};
+    }
+  }
+  // lane (lx, lk) holds rows 4 lk + i, i = 0..3, of column n0 + 16 c + lx
+#pragma unroll
+  for (int c = 0; c < R / 16; ++c) {
+    const int n = (int)n0 + 16 * c + lx;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * lk + i;
+      if (m >= M) continue;
+      if (p.slices > 1)
+        p.part[((int64_t)s * M + m) * N + n] = acc[c][i];
+      else
+        skinny_store(p, m, n, acc[c][i]);
+    }
   }
 }
 

@@ -901,15 +901,15 @@ mm_status run_empty_k(const Request& r, void* stream) {
 // ----------------------------------------------------------------------------
 // Skinny products (gemm_skinny): K-contiguous single-weight single-output
 // products of at most 16 rows against at least 8 MiB of weights, unless a
-// configuration is forced.  Without a workspace each 16-column block is one
-// workgroup; with one, K is also cut into S slices (at least 512 k each, at
-// most 16) so that about 1024 workgroups stream the weights.
+// configuration is forced.  Without a workspace each block of 32 weight rows
+// is one workgroup; with one, K may also be cut into S slices (at most 16, of
+// at least one 512-k stage each) when that fills the CUs better.
 // ----------------------------------------------------------------------------
-constexpr int64_t kSkinnyTargetWgs = 1024;
+constexpr int64_t kSkinnyCUs = 256;  // workgroups resident at once: one per CU (LDS)
 
 bool skinny_shape(const Request& r) {
   return a_kcontig(r.layout) && b_kcontig(r.layout) && !r.ffn && !r.out_pre && r.batch == 1 &&
-         r.M <= mmk::kSkinnyMaxM && r.K >= 256 && r.N * r.K >= (int64_t(1) << 22);
+         r.M <= mmk::kSkinnyMaxM && r.K >= 256 && r.K <= (int64_t(1) << 24) && r.N * r.K >= (int64_t(1) << 22);
 }
 
 struct SkinnyPlan {
@@ -917,16 +917,29 @@ struct SkinnyPlan {
   int slices = 1;   // S
 };
 
+// The number of slices S (at most max_slices) that minimises the modelled
+// time: rounds of resident workgroups times the stages each streams, plus,
+// when split, the second launch (about as long as streaming 12.5 MB) and
+// the partial sums' traffic, in units of one round of stages (256
+// workgroups' stage of weights).
 SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
+  const int64_t ngroups = cdiv(r.N, mmk::kSkinnyRows);
+  const int64_t smax = std::min<int64_t>({16, max_slices, std::max<int64_t>(1, r.K / mmk::kSkinnyKD)});
   SkinnyPlan sp;
-  int64_t S = 1;
-  if (max_slices > 1) {
-    S = cdiv(kSkinnyTargetWgs, cdiv(r.N, 16));
-    S = std::min<int64_t>({S, r.K / 512, 16, max_slices});
-    if (S < 1) S = 1;
+  double best = -1.0;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t kc = cdiv(cdiv(r.K, S), 64) * 64;
+    const int64_t slices = cdiv(r.K, kc);
+    if (slices != S) continue;
+    double cost = (double)cdiv(ngroups * slices, kSkinnyCUs) * (double)kc / mmk::kSkinnyKD;
+    if (slices > 1)
+      cost += (12.5e6 + 2.0 * (double)(slices * r.M * r.N * 4)) / (kSkinnyCUs * 2.0 * mmk::kSkinnyRows * mmk::kSkinnyKD);
+    if (best < 0.0 || cost < best - 1e-9) {
+      best = cost;
+      sp.kc = (int)kc;
+      sp.slices = (int)slices;
+    }
   }
-  sp.kc = (int)(cdiv(cdiv(r.K, S), 32) * 32);
-  sp.slices = (int)cdiv(r.K, sp.kc);
   return sp;
 }
 
@@ -956,7 +969,7 @@ mm_status run_skinny(const Request& r, void* stream) {
   p.slices = sp.slices;
   p.epi = r.epi;
   p.out_f32 = r.out_f32 ? 1 : 0;
-  const int64_t grid = cdiv(r.N, 16) * sp.slices;
+  const int64_t grid = cdiv(r.N, mmk::kSkinnyRows) * sp.slices;
   void* args[] = {&p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::gemm_skinny), dim3((unsigned)grid), dim3(256),
                                  args, 0, static_cast<hipStream_t>(stream));
@@ -1249,7 +1262,7 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
     // the skinny kernel (no device query): S slices of K with a workspace
     kernel = "gemm_skinny";
     const SkinnyPlan sp = skinny_plan(rq, 16);
-    if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx16,", sp.slices);
+    if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx%d,", sp.slices, mmk::kSkinnyRows);
   } else if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
               false, false};

@@ -74,7 +74,7 @@ def test_graph_replays_equal_eager_calls(dev):
     Wr = synth.randn_bf16((Nr, Kr), Kr ** -0.5, 811).to(dev)
     br = synth.randn_bf16((Nr,), 1.0, 812).to(dev)
     y6 = torch.empty((Mr, Nr), dtype=torch.bfloat16, device=dev)
-    Mk, Nk, Kk = 16, 8192, 4096
+    Mk, Nk, Kk = 16, 4096, 8192
     assert binding.describe_config("linear", Mk, Nk, Kk).endswith("KERNEL=gemm_skinny")
     xk = synth.randn_bf16((Mk, Kk), 1.0, 813).to(dev)
     Wk = synth.randn_bf16((Nk, Kk), Kk ** -0.5, 814).to(dev)

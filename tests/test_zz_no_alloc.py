@@ -51,9 +51,9 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 # 64 MiB of scratch; then 12 tiles in 10 chunks: 120 slots); then a stored-[K][N] product
 # (256 x 256 tiles), a shape that runs unsplit, one whose K is not a
 # multiple of 64 (never split: the slab kernel's ragged instance), and a
-# skinny product (16 rows: its fp32 partial outputs of 2 slices of K)
+# skinny product (16 rows: its fp32 partial outputs of 4 slices of K)
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
-            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt"), (16, 8192, 4096, "nt")]
+            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt"), (16, 4096, 8192, "nt")]
 UNSPLIT = {(520, 392, 512), (2900, 3000, 1032)}
 
 
