@@ -55,7 +55,8 @@ CSRC = os.path.join(ROOT, "dense_bf16_gemm_amd", "csrc")
 
 # the headers the benchmarked workloads' kernels are built from, and the host
 # code that chooses their tile order and launch
-SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp", "gemm_small.hpp", "mm_api.hip")
+SLAB_SOURCES = ("gemm_kernel.hpp", "gemm_nt_pipe.hpp", "gemm_nt_slab.hpp", "gemm_skinny.hpp", "gemm_small.hpp",
+                "mm_api.hip")
 
 
 def kernel_source_hash() -> str:
@@ -295,10 +296,16 @@ def main() -> int:
     ffn = str(w.form == "ffn").lower()
     # the workspace the step passes ("auto") turns under-filled products into
     # split-K: the slab kernel's split-K instance, then splitk_reduce
-    splitk = w.form != "ffn" and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0
+    skinny = cfg["KERNEL"] == "gemm_skinny"
+    splitk = not skinny and w.form != "ffn" and binding.workspace_size(w.form, w.M, w.N, w.K, w.layout) > 0
     bkn = str(w.layout in ("nn", "tn")).lower()
     amk = str(w.layout in ("tn", "tt")).lower()
-    if splitk:
+    if skinny:
+        # at most 16 rows: bound by reading the weight once; with the step's
+        # workspace K may be cut into slices (SPLIT=<slices>x<weight rows>)
+        kernel = "mmk::gemm_skinny" + (" + mmk::skinny_reduce" if "SPLIT" in cfg else "")
+        tiles = f"ROWS=64,SLICES={cfg.get('SPLIT', '1x64').split('x')[0]},KERNEL=gemm_skinny"
+    elif splitk:
         # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights,
         # [K][M] activations, bias staged in LDS, ragged K>;
         # SPLIT=<chunks>x<tile width>
@@ -368,6 +375,13 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if skinny:
+        # the weight read once bounds it: algorithmic bytes per launch over
+        # the mean launch time, against the 8 TB/s of HBM
+        gbs = w.algorithmic_bytes / (mean_launch * 1e-3) / 1e9
+        result["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "bytes_per_launch": w.algorithmic_bytes})
     print(f"bench: {name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
           f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of peak), wall {wall:.3f} s", file=sys.stderr,
           flush=True)

@@ -924,7 +924,8 @@ struct SkinnyPlan {
 // workgroups' stage of weights).
 SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
   const int64_t ngroups = cdiv(r.N, mmk::kSkinnyRows);
-  const int64_t smax = std::min<int64_t>({16, max_slices, std::max<int64_t>(1, r.K / mmk::kSkinnyKD)});
+  const int64_t smax =
+      std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, std::max<int64_t>(1, r.K / mmk::kSkinnyKD)});
   SkinnyPlan sp;
   double best = -1.0;
   for (int64_t S = 1; S <= smax; ++S) {
@@ -950,7 +951,7 @@ int64_t skinny_ws_bytes(const Request& r, const SkinnyPlan& sp) {
 mm_status run_skinny(const Request& r, void* stream) {
   // with the static scratch, as many slices as it holds
   const int64_t per_slice = r.M * r.N * 4;
-  SkinnyPlan sp = skinny_plan(r, r.ws ? (r.static_ws ? r.ws_bytes / per_slice : 16) : 1);
+  SkinnyPlan sp = skinny_plan(r, r.ws ? (r.static_ws ? r.ws_bytes / per_slice : mmk::kSkinnyMaxSlices) : 1);
   const int64_t need = skinny_ws_bytes(r, sp);
   if (need > 0) {
     if (r.ws_bytes < need) return fail(MM_ERR_INVALID_VALUE, "workspace smaller than mm_workspace_size reports");
@@ -975,7 +976,7 @@ mm_status run_skinny(const Request& r, void* stream) {
                                  args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny): ") + hipGetErrorString(e));
   if (sp.slices > 1) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::skinny_reduce), dim3((unsigned)cdiv(r.M * r.N, 256)),
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::skinny_reduce), dim3((unsigned)cdiv(r.M * r.N, 1024)),
                         dim3(256), args, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
       return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny reduction): ") + hipGetErrorString(e));
@@ -1147,7 +1148,7 @@ mm_status mm_workspace_size(int form, int64_t M, int64_t N, int64_t K, mm_layout
   if (M == 0 || N == 0 || K == 0) return MM_OK;
   const Config c = choose_config_for(r);
   if (!c.forced && skinny_shape(r)) {
-    *bytes = skinny_ws_bytes(r, skinny_plan(r, 16));
+    *bytes = skinny_ws_bytes(r, skinny_plan(r, mmk::kSkinnyMaxSlices));
     return MM_OK;
   }
   if (!splitk_shape(r) || c.sk == 1) return MM_OK;
@@ -1261,7 +1262,7 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
   if (skinny) {
     // the skinny kernel (no device query): S slices of K with a workspace
     kernel = "gemm_skinny";
-    const SkinnyPlan sp = skinny_plan(rq, 16);
+    const SkinnyPlan sp = skinny_plan(rq, mmk::kSkinnyMaxSlices);
     if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx%d,", sp.slices, mmk::kSkinnyRows);
   } else if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,

@@ -130,12 +130,17 @@ WORKLOADS: Dict[str, Workload] = {
 # Shapes measured for one design question each (bench.py --workload), not
 # parity workloads: an 8192 x 8192 output (four tiles per workgroup) with
 # K = 65536, whose 32 MiB K panels are far larger than an XCD's 4 MiB L2 --
-# where the direction of each tile's K loop could matter.
+# where the direction of each tile's K loop could matter; and a decode-step
+# product (16 activation rows against a 448 MiB weight, larger than the
+# 256 MiB last-level cache), bound by reading the weight once.
 EXTRA_WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
         Workload("matmul_nt_8192x8192x65536", "matmul", 8192, 8192, 65536, "nt", "none", "bf16",
                  (TensorSpec("A", (8192, 65536), 1.0, 701), TensorSpec("Bt", (8192, 65536), 2.0 ** -8, 702))),
+        Workload("linear_bias_decode_16x28672x8192", "linear", 16, 28672, 8192, "nt", "bias", "bf16",
+                 (TensorSpec("x", (16, 8192), 1.0, 801), TensorSpec("W", (28672, 8192), 8192 ** -0.5, 802),
+                  TensorSpec("bias", (28672,), 1.0, 803))),
     ]
 }
 

@@ -939,9 +939,10 @@ def test_batched_ragged_k_slab(dev, layout):
 
 # ------------------------------------------------------------ skinny products
 # (M, N, K): at most 16 activation rows against at least 8 MiB of weights --
-# ragged N and K (multiples of 8), slices of K that end mid-step, one row
+# ragged N and K (multiples of 8), slices of K that end mid-stage, one row,
+# an M*N that is not a multiple of 4 (the reduction's scalar path)
 SKINNY_SHAPES = [(1, 4096, 1024), (7, 1000, 8200), (16, 8192, 1032), (9, 4104, 4096), (16, 2048, 2056),
-                 (13, 3000, 4096), (2, 1032, 8192)]
+                 (13, 3000, 4096), (2, 1032, 8192), (7, 1001, 8200)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_SHAPES)
