@@ -1,5 +1,5 @@
-// Skinny products: at most 16 rows of activations against a large weight
-// (the decode step of a served model at small batch: x [M][K], M <= 16,
+// Skinny products: at most 32 rows of activations against a large weight
+// (the decode step of a served model at small batch: x [M][K], M <= 32,
 // W [N][K]).
 //
 // Such a product is bound by reading W once from HBM; its MFMA work is small.
@@ -7,10 +7,10 @@
 // on rows past M, so here a workgroup takes 64 of W's rows (64 output
 // columns) and streams them once through a ring of three LDS stages of 256
 // k.  Each wave-wide copy fills two rows' 512-byte runs straight from
-// memory into LDS (buffer loads to LDS: no registers), the 16 activation
-// rows of the stage come the same way, and the four waves each multiply a
-// quarter of the stage's k-steps with MFMAs whose fragments are read from
-// LDS; the waves' parts meet in LDS in a fixed order at the end.  With a
+// memory into LDS (buffer loads to LDS: no registers), the 16 or 32
+// activation rows of the stage come the same way, and the four waves each
+// multiply a quarter of the stage's k-steps with MFMAs whose fragments are
+// read from LDS; the waves' parts meet in LDS in a fixed order at the end.  With a
 // workspace K may also be cut into S slices (when that fills the CUs
 // better): each writes its fp32 sums to slice s of the workspace and
 // skinny_reduce adds the slices in k order.  Results: fp32 sums of the bf16
@@ -27,7 +27,11 @@
 // 43 -> 32.9 (28.8).  Not kept: 32-row groups with 512-k stages (one row per
 // copy; 33-35 us at 8192 x 8192, 115 us at 28672 x 8192), 48-row groups,
 // four or five stages (no gain), and rotating each workgroup's first stage
-// (faster at 14336 x 4096, 6 us slower at 8192 x 8192).
+// (faster at 14336 x 4096, 6 us slower at 8192 x 8192).  Rows 17-32 (two
+// activation blocks, 48 KiB stages): 24 x 8192 x 8192 49.0 -> 35.9 us and
+// 32 x 14336 x 4096 47.7 -> 30.9 against the tile kernels (BLAS 30.0, 26.2),
+// but 32 x 28672 x 8192 106.6 -> 114.4.  Four blocks (64 rows, two 64 KiB
+// stages) lost to the tile kernels: 64 x 28672 x 8192 112.9 -> 134.3 us.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -48,12 +52,14 @@ struct SkinnyParams {
   int out_f32;
 };
 
-constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxM = 32;
 constexpr int kSkinnyRows = 64;    // weight rows (output columns) per workgroup
 constexpr int kSkinnyKD = 256;     // k per stage: 512-byte runs, two rows per copy
-constexpr int kSkinnyStages = 3;   // ring of stages in LDS (120 KiB)
 constexpr int kSkinnyMaxSlices = 16;
-constexpr int kSkinnyStageBytes = (kSkinnyRows + kSkinnyMaxM) * kSkinnyKD * 2;
+// Stages in the LDS ring for XB blocks of 16 activation rows: three, of 40
+// KiB for one block and 48 KiB for two.
+__host__ __device__ constexpr int skinny_stages(int) { return 3; }
+__host__ __device__ constexpr int skinny_stage_bytes(int xb) { return (kSkinnyRows + 16 * xb) * kSkinnyKD * 2; }
 
 // s_waitcnt for the copies of `ahead` stages (at most A) left in flight
 template <int PER, int A>
@@ -78,13 +84,17 @@ __device__ __forceinline__ void skinny_store(const SkinnyParams& p, int m, int n
     reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
+// XB: blocks of 16 activation rows (M <= 16 XB)
+template <int XB>
 __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
-  constexpr int R = kSkinnyRows, KD = kSkinnyKD, NS = kSkinnyStages, SB = kSkinnyStageBytes;
+  constexpr int R = kSkinnyRows, KD = kSkinnyKD, NS = skinny_stages(XB), SB = skinny_stage_bytes(XB);
+  constexpr int XM = 16 * XB;           // activation rows in a stage
   constexpr int P = KD * 2;             // bytes of a row in a stage
   constexpr int CPR = KD / 8;           // 16-byte chunks of a row in a stage
   constexpr int RPI = 64 / CPR;         // rows per wave-wide copy
-  constexpr int WC = R / RPI / 4, XC = kSkinnyMaxM / RPI / 4;  // copies per wave and stage
-  static_assert(CPR >= 16 && CPR <= 64 && R % (4 * RPI) == 0 && kSkinnyMaxM % (4 * RPI) == 0, "stage shape");
+  constexpr int WC = R / RPI / 4, XC = XM / RPI / 4;  // copies per wave and stage
+  static_assert(CPR >= 16 && CPR <= 64 && R % (4 * RPI) == 0 && XM % (4 * RPI) == 0, "stage shape");
+  static_assert(NS * SB <= 160 * 1024 && 3 * XB * (R / 16) * 1024 <= NS * SB, "LDS");
   constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
   constexpr uint32_t kOob = 0x80000000u;  // past every record count below
   __shared__ __attribute__((aligned(1024))) char smem[NS * SB];
@@ -103,7 +113,7 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
   const int kend = min(K, kbeg + p.kc);
   const int nst = (kend - kbeg + KD - 1) / KD;
 
-  // Copies: a stage holds KD k of the group's R weight rows and of the 16
+  // Copies: a stage holds KD k of the group's R weight rows and of the XM
   // activation rows; each wave-wide LDS copy fills RPI rows of it.  The
   // lane that fills chunk position c of row r fetches the row's 16-byte
   // chunk c ^ (r & 15), so that the fragment reads of 16 rows at one chunk
@@ -157,20 +167,26 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
 
   // wave w multiplies k-steps w*KS .. w*KS+KS-1 (32 k each) of every stage
   constexpr int KS = KD / 128;
-  f32x4 acc[R / 16];
+  // acc[b * CB + c]: activation block b against weight block c
+  constexpr int CB = R / 16, NA = XB * CB;
+  f32x4 acc[NA];
 #pragma unroll
-  for (int c = 0; c < R / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int st) __attribute__((always_inline)) {
     const char* slot = smem + (st % NS) * SB;
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
       const int pos = ((4 * (KS * wave + q) + lk) ^ lx) * 16;
-      const u32x4 xf = *reinterpret_cast<const u32x4*>(slot + (R + lx) * P + pos);
+      u32x4 xf[XB];
 #pragma unroll
-      for (int c = 0; c < R / 16; ++c) {
+      for (int b = 0; b < XB; ++b) xf[b] = *reinterpret_cast<const u32x4*>(slot + (R + 16 * b + lx) * P + pos);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
         const u32x4 wf = *reinterpret_cast<const u32x4*>(slot + (16 * c + lx) * P + pos);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf),
-                                                         __builtin_bit_cast(bf16x8, wf), acc[c], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < XB; ++b)
+          acc[b * CB + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xf[b]), __builtin_bit_cast(bf16x8, wf), acc[b * CB + c], 0, 0, 0);
       }
     }
   };
@@ -197,31 +213,35 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
   f32x4* red = reinterpret_cast<f32x4*>(smem);
   if (wave > 0) {
 #pragma unroll
-    for (int c = 0; c < R / 16; ++c) red[((wave - 1) * (R / 16) + c) * 64 + lane] = acc[c];
+    for (int a = 0; a < NA; ++a) red[((wave - 1) * NA + a) * 64 + lane] = acc[a];
   }
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
 #pragma unroll
-    for (int c = 0; c < R / 16; ++c) {
-      const f32x4 v = red[(q * (R / 16) + c) * 64 + lane];
-      acc[c] = f32x4{acc[c][0] + v[0], acc[c][1] + v[1], acc[c][2] + v[2], acc[c][3] + v[3]};
+    for (int a = 0; a < NA; ++a) {
+      const f32x4 v = red[(q * NA + a) * 64 + lane];
+      acc[a] = f32x4{acc[a][0] + v[0], acc[a][1] + v[1], acc[a][2] + v[2], acc[a][3] + v[3]};
     }
   }
-  // lane (lx, lk) holds rows 4 lk + i, i = 0..3, of column n0 + 16 c + lx
+  // lane (lx, lk) holds rows 16 b + 4 lk + i, i = 0..3, of column
+  // n0 + 16 c + lx
 #pragma unroll
-  for (int c = 0; c < R / 16; ++c) {
+  for (int c = 0; c < CB; ++c) {
     const int n = (int)n0 + 16 * c + lx;
     if (n >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * lk + i;
-      if (m >= M) continue;
-      if (p.slices > 1)
-        p.part[((int64_t)s * M + m) * N + n] = acc[c][i];
-      else
-        skinny_store(p, m, n, acc[c][i]);
+    for (int b = 0; b < XB; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * lk + i;
+        if (m >= M) continue;
+        if (p.slices > 1)
+          p.part[((int64_t)s * M + m) * N + n] = acc[b * CB + c][i];
+        else
+          skinny_store(p, m, n, acc[b * CB + c][i]);
+      }
     }
   }
 }

@@ -900,7 +900,7 @@ mm_status run_empty_k(const Request& r, void* stream) {
 
 // ----------------------------------------------------------------------------
 // Skinny products (gemm_skinny): K-contiguous single-weight single-output
-// products of at most 16 rows against at least 8 MiB of weights, unless a
+// products of at most 32 rows against at least 8 MiB of weights, unless a
 // configuration is forced.  Without a workspace each block of 32 weight rows
 // is one workgroup; with one, K may also be cut into S slices (at most 16, of
 // at least one 512-k stage each) when that fills the CUs better.
@@ -972,8 +972,10 @@ mm_status run_skinny(const Request& r, void* stream) {
   p.out_f32 = r.out_f32 ? 1 : 0;
   const int64_t grid = cdiv(r.N, mmk::kSkinnyRows) * sp.slices;
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::gemm_skinny), dim3((unsigned)grid), dim3(256),
-                                 args, 0, static_cast<hipStream_t>(stream));
+  // blocks of 16 activation rows the kernel carries
+  const void* kern = r.M <= 16 ? reinterpret_cast<const void*>(&mmk::gemm_skinny<1>)
+                               : reinterpret_cast<const void*>(&mmk::gemm_skinny<2>);
+  hipError_t e = hipLaunchKernel(kern, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny): ") + hipGetErrorString(e));
   if (sp.slices > 1) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&mmk::skinny_reduce), dim3((unsigned)cdiv(r.M * r.N, 1024)),

@@ -163,7 +163,7 @@ mm_status mm_linear_batched(const void* x, const void* W, const void* bias, void
  * each, or equal contiguous ranges: stream-K); each piece leaves its fp32
  * partial tile in this workspace (one 256 KiB slot per workgroup, two per
  * stream-K workgroup), and a second kernel on the same stream adds them in k
- * order and applies the epilogue once.  Products of at most 16 rows (the
+ * order and applies the epilogue once.  Products of at most 32 rows (the
  * skinny kernel, see mm_describe_config) use it for fp32 partial outputs of
  * S slices of K (S x M x N x 4 bytes), added in k order the same way.
  *   form    0 matmul/linear, 1 FFN (never uses a workspace)
@@ -252,7 +252,7 @@ mm_status mm_set_config(const char* spec);
  * and KERNEL parts describe a call without a workspace; with SPLIT present,
  * a call given a workspace (mm_matmul_ws, mm_linear_ws, mm_matmul_noalloc)
  * runs the slab kernel on 256 x <tile width> tiles instead.  Products of at
- * most 16 rows against at least 8 MiB of weights (layout MM_NT, one weight,
+ * most 32 rows against at least 8 MiB of weights (layout MM_NT, one weight,
  * no forced configuration, K at most 2^24) name gemm_skinny, with
  * SPLIT=<k slices>x32 (32 weight rows per workgroup) when a workspace would
  * cut K (no device query).  K = 0 names empty_k_fill.  form: 0 matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE

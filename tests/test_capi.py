@@ -160,7 +160,7 @@ def test_heuristic_choices():
 
 
 def test_skinny_choices():
-    """At most 16 rows against at least 8 MiB of weights take the skinny
+    """At most 32 rows against at least 8 MiB of weights take the skinny
     kernel (64 weight rows per workgroup); the slice count is the modelled
     best: none where 64-row groups already fill the CUs more than once,
     slices where they leave CUs idle."""
@@ -168,9 +168,11 @@ def test_skinny_choices():
     assert binding.describe_config("linear", 16, 14336, 4096).endswith("PIPE=3,KERNEL=gemm_skinny")
     assert binding.describe_config("linear", 16, 4096, 14336).endswith("SPLIT=4x64,KERNEL=gemm_skinny")
     assert binding.describe_config("linear", 1, 4096, 1024).endswith("KERNEL=gemm_skinny")
-    # 17 rows, stored-[K][N] weights, an FFN pair, too little weight, K past
+    assert binding.describe_config("linear", 17, 8192, 8192).endswith("KERNEL=gemm_skinny")
+    assert binding.describe_config("linear", 32, 14336, 4096).endswith("KERNEL=gemm_skinny")
+    # 33 rows, stored-[K][N] weights, an FFN pair, too little weight, K past
     # 2^24: the tile kernels
-    assert not binding.describe_config("linear", 17, 8192, 8192).endswith("gemm_skinny")
+    assert not binding.describe_config("linear", 33, 8192, 8192).endswith("gemm_skinny")
     assert not binding.describe_config("matmul", 16, 8192, 8192, "nn").endswith("gemm_skinny")
     assert not binding.describe_config("ffn", 16, 8192, 8192).endswith("gemm_skinny")
     assert not binding.describe_config("linear", 16, 1024, 2048).endswith("gemm_skinny")

@@ -938,11 +938,13 @@ def test_batched_ragged_k_slab(dev, layout):
 
 
 # ------------------------------------------------------------ skinny products
-# (M, N, K): at most 16 activation rows against at least 8 MiB of weights --
+# (M, N, K): at most 32 activation rows against at least 8 MiB of weights --
 # ragged N and K (multiples of 8), slices of K that end mid-stage, one row,
-# an M*N that is not a multiple of 4 (the reduction's scalar path)
+# an M*N that is not a multiple of 4 (the reduction's scalar path); one and
+# two blocks of 16 activation rows, full and partial
 SKINNY_SHAPES = [(1, 4096, 1024), (7, 1000, 8200), (16, 8192, 1032), (9, 4104, 4096), (16, 2048, 2056),
-                 (13, 3000, 4096), (2, 1032, 8192), (7, 1001, 8200)]
+                 (13, 3000, 4096), (2, 1032, 8192), (7, 1001, 8200), (17, 4104, 4096), (32, 2048, 2056),
+                 (27, 1001, 8200), (32, 8192, 1032)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_SHAPES)
@@ -981,7 +983,7 @@ def test_skinny_mapping_bitexact(dev, shape, ws):
     np.testing.assert_array_equal(out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("shape", [(16, 8192, 8192), (5, 4096, 4104)])
+@pytest.mark.parametrize("shape", [(16, 8192, 8192), (5, 4096, 4104), (32, 4096, 8192), (29, 8192, 4096)])
 @pytest.mark.parametrize("epi", ["bias_gelu_tanh", "gelu_tanh", "none"])
 def test_skinny_random(dev, shape, epi):
     """Random operands through mm.linear (its automatic workspace: K in
