@@ -53,13 +53,15 @@ struct SkinnyParams {
 };
 
 constexpr int kSkinnyMaxM = 32;
-constexpr int kSkinnyRows = 64;    // weight rows (output columns) per workgroup
-constexpr int kSkinnyKD = 256;     // k per stage: 512-byte runs, two rows per copy
 constexpr int kSkinnyMaxSlices = 16;
-// Stages in the LDS ring for XB blocks of 16 activation rows: three, of 40
-// KiB for one block and 48 KiB for two.
+// Per XB (blocks of 16 activation rows): weight rows per workgroup, k per
+// stage (256: 512-byte runs, two rows per copy) and stages in the LDS ring
+// (three, of 40 KiB for one block and 48 KiB for two).
+__host__ __device__ constexpr int skinny_xb(int m) { return m <= 16 ? 1 : 2; }
+__host__ __device__ constexpr int skinny_rows(int) { return 64; }
+__host__ __device__ constexpr int skinny_kd(int) { return 256; }
 __host__ __device__ constexpr int skinny_stages(int) { return 3; }
-__host__ __device__ constexpr int skinny_stage_bytes(int xb) { return (kSkinnyRows + 16 * xb) * kSkinnyKD * 2; }
+__host__ __device__ constexpr int skinny_stage_bytes(int xb) { return (skinny_rows(xb) + 16 * xb) * skinny_kd(xb) * 2; }
 
 // s_waitcnt for the copies of `ahead` stages (at most A) left in flight
 template <int PER, int A>
@@ -87,7 +89,7 @@ __device__ __forceinline__ void skinny_store(const SkinnyParams& p, int m, int n
 // XB: blocks of 16 activation rows (M <= 16 XB)
 template <int XB>
 __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
-  constexpr int R = kSkinnyRows, KD = kSkinnyKD, NS = skinny_stages(XB), SB = skinny_stage_bytes(XB);
+  constexpr int R = skinny_rows(XB), KD = skinny_kd(XB), NS = skinny_stages(XB), SB = skinny_stage_bytes(XB);
   constexpr int XM = 16 * XB;           // activation rows in a stage
   constexpr int P = KD * 2;             // bytes of a row in a stage
   constexpr int CPR = KD / 8;           // 16-byte chunks of a row in a stage

@@ -923,18 +923,19 @@ struct SkinnyPlan {
 // the partial sums' traffic, in units of one round of stages (256
 // workgroups' stage of weights).
 SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
-  const int64_t ngroups = cdiv(r.N, mmk::kSkinnyRows);
-  const int64_t smax =
-      std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, std::max<int64_t>(1, r.K / mmk::kSkinnyKD)});
+  const int xb = mmk::skinny_xb((int)r.M);
+  const int64_t rows = mmk::skinny_rows(xb), kd = mmk::skinny_kd(xb);
+  const int64_t ngroups = cdiv(r.N, rows);
+  const int64_t smax = std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, std::max<int64_t>(1, r.K / kd)});
   SkinnyPlan sp;
   double best = -1.0;
   for (int64_t S = 1; S <= smax; ++S) {
     const int64_t kc = cdiv(cdiv(r.K, S), 64) * 64;
     const int64_t slices = cdiv(r.K, kc);
     if (slices != S) continue;
-    double cost = (double)cdiv(ngroups * slices, kSkinnyCUs) * (double)kc / mmk::kSkinnyKD;
+    double cost = (double)cdiv(ngroups * slices, kSkinnyCUs) * (double)kc / (double)kd;
     if (slices > 1)
-      cost += (12.5e6 + 2.0 * (double)(slices * r.M * r.N * 4)) / (kSkinnyCUs * 2.0 * mmk::kSkinnyRows * mmk::kSkinnyKD);
+      cost += (12.5e6 + 2.0 * (double)(slices * r.M * r.N * 4)) / (kSkinnyCUs * 2.0 * (double)(rows * kd));
     if (best < 0.0 || cost < best - 1e-9) {
       best = cost;
       sp.kc = (int)kc;
@@ -970,11 +971,12 @@ mm_status run_skinny(const Request& r, void* stream) {
   p.slices = sp.slices;
   p.epi = r.epi;
   p.out_f32 = r.out_f32 ? 1 : 0;
-  const int64_t grid = cdiv(r.N, mmk::kSkinnyRows) * sp.slices;
+  const int xb = mmk::skinny_xb((int)r.M);
+  const int64_t grid = cdiv(r.N, mmk::skinny_rows(xb)) * sp.slices;
   void* args[] = {&p};
   // blocks of 16 activation rows the kernel carries
-  const void* kern = r.M <= 16 ? reinterpret_cast<const void*>(&mmk::gemm_skinny<1>)
-                               : reinterpret_cast<const void*>(&mmk::gemm_skinny<2>);
+  const void* kern = xb == 1 ? reinterpret_cast<const void*>(&mmk::gemm_skinny<1>)
+                              : reinterpret_cast<const void*>(&mmk::gemm_skinny<2>);
   hipError_t e = hipLaunchKernel(kern, dim3((unsigned)grid), dim3(256), args, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MM_ERR_HIP, std::string("hipLaunchKernel (skinny): ") + hipGetErrorString(e));
   if (sp.slices > 1) {
@@ -1265,7 +1267,8 @@ mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layou
     // the skinny kernel (no device query): S slices of K with a workspace
     kernel = "gemm_skinny";
     const SkinnyPlan sp = skinny_plan(rq, mmk::kSkinnyMaxSlices);
-    if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx%d,", sp.slices, mmk::kSkinnyRows);
+    if (sp.slices > 1) std::snprintf(split, sizeof split, "SPLIT=%dx%d,", sp.slices,
+                                        mmk::skinny_rows(mmk::skinny_xb((int)M)));
   } else if (M > 0 && N > 0 && K > 0 && form == 0 && c.sk != 1) {
     Request r{nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, (int)layout, mmk::EPI_NONE,
               false, false};
