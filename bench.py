@@ -83,7 +83,7 @@ def traffic_from_profile(workload: str):
 
 def sclk_path():
     """The driver's GFX clock table (pp_dpm_sclk; its starred line is the
-    current clock) when exactly one card exposes one (a one-GPU machine)."""
+    current clock) when exactly one card exposes one (a single-GPU machine)."""
     paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
     return paths[0] if len(paths) == 1 else None
 
