@@ -303,7 +303,8 @@ def main() -> int:
     if skinny:
         # at most 16 rows: bound by reading the weight once; with the step's
         # workspace K may be cut into slices (SPLIT=<slices>x<weight rows>)
-        kernel = "mmk::gemm_skinny" + (" + mmk::skinny_reduce" if "SPLIT" in cfg else "")
+        kernel = (f"mmk::gemm_skinny<{1 if w.M <= 16 else 2}>" +
+                  (" + mmk::skinny_reduce" if "SPLIT" in cfg else ""))
         tiles = f"ROWS=64,SLICES={cfg.get('SPLIT', '1x64').split('x')[0]},KERNEL=gemm_skinny"
     elif splitk:
         # <tile, waves, FFN, split-K, pre-activation output, [K][N] weights,
