@@ -1076,6 +1076,34 @@ def test_nonfinite_inputs(dev, case, epi):
     assert excess.max() <= 0
 
 
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("epi", ["none", "bias_gelu_tanh"])
+def test_nonfinite_inputs_skinny(dev, ws, epi):
+    """The same classes through the skinny kernel: 13 rows (one block of 16)
+    and 29 (two), unsplit and with K in slices (fp32 partial sums added by
+    the reduction: +inf in one slice and -inf in another give NaN)."""
+    binding.set_config(None)
+    for (M, N, K) in [(13, 4104, 2056), (29, 2056, 4104)]:
+        say("non-finite skinny", (M, N, K), epi, "ws" if ws else "no ws")
+        assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_skinny")
+        A, B, cls = nonfinite_case(M, N, K, "nt", 47 + M)
+        bias = synth.randn_bf16((N,), 1.0, 49)
+        nbytes = binding.workspace_size("linear", M, N, K)
+        assert nbytes > 0 or not ws, "shape no longer split"
+        wsp = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if ws else None
+        out = mm.linear(A.to(dev), B.to(dev), bias.to(dev), epi, workspace=wsp)
+        torch.cuda.synchronize()
+        y, bits = oracle.gemm(synth.bits(A), synth.bits(B), "nt", epi, bias=synth.bits(bias))
+        ref = (bits.astype(np.uint32) << 16).view(np.float32)
+        got = out.float().cpu().numpy()
+        if epi == "none":
+            np.testing.assert_array_equal(value_class(ref), cls)
+        np.testing.assert_array_equal(value_class(got), value_class(ref))
+        fin = value_class(ref) == 0
+        excess = np.abs(got[fin].astype(np.float64) - y[fin]) - 2e-2 * (np.abs(y[fin]) + 1.0)
+        assert excess.max() <= 0
+
+
 def test_nonfinite_inputs_split_and_ffn(dev):
     """The same classes through split-K (partial tiles added by the
     reduction) and through the FFN's SwiGLU (SiLU(-inf) u is NaN)."""
