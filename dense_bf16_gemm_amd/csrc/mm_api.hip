@@ -926,7 +926,9 @@ SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
   const int xb = mmk::skinny_xb((int)r.M);
   const int64_t rows = mmk::skinny_rows(xb), kd = mmk::skinny_kd(xb);
   const int64_t ngroups = cdiv(r.N, rows);
-  const int64_t smax = std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, std::max<int64_t>(1, r.K / kd)});
+  // one slice (no workspace) is always possible
+  const int64_t smax =
+      std::max<int64_t>(1, std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, r.K / kd}));
   SkinnyPlan sp;
   double best = -1.0;
   for (int64_t S = 1; S <= smax; ++S) {

@@ -50,11 +50,13 @@ def with_ws(A, B, M, N, K, layout, out_f32, out):
 # automatic rule (32 tiles of 256 x 128 in 8 chunks: 256 slots, the whole
 # 64 MiB of scratch; then 12 tiles in 10 chunks: 120 slots); then a stored-[K][N] product
 # (256 x 256 tiles), a shape that runs unsplit, one whose K is not a
-# multiple of 64 (never split: the slab kernel's ragged instance), and a
-# skinny product (16 rows: its fp32 partial outputs of 4 slices of K)
+# multiple of 64 (never split: the slab kernel's ragged instance), a skinny
+# product (16 rows: its fp32 partial outputs of 4 slices of K), and a skinny
+# product whose one slice of partial outputs (67 MB) would not fit the
+# scratch: it runs unsplit
 SEQUENCE = [(1000, 900, 16384, "nt"), (520, 395, 8192, "nt"), (304, 264, 8192, "nn"),
-            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt"), (16, 4096, 8192, "nt")]
-UNSPLIT = {(520, 392, 512), (2900, 3000, 1032)}
+            (520, 392, 512, "nt"), (2900, 3000, 1032, "nt"), (16, 4096, 8192, "nt"), (32, 524296, 256, "nt")]
+UNSPLIT = {(520, 392, 512), (2900, 3000, 1032), (32, 524296, 256)}
 
 
 @pytest.mark.parametrize("out_f32", [True, False])
