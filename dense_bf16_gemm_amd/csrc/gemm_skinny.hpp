@@ -123,6 +123,8 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
   // descriptors' record counts and read as zeros; chunks past the slice's
   // end are pushed past them.
   const uint64_t rec_w64 = (uint64_t)(N - n0) * (uint64_t)K * 2u;
+  // (clamped below bit 31: with K <= 2^23 the group's own rows end below
+  // 2^30, far inside the clamped count at every k0)
   const uint32_t rec_w = rec_w64 > 0x7fffffffull ? 0x7fffffffu : (uint32_t)rec_w64;
   const uint32_t rec_x = (uint32_t)M * (uint32_t)K * 2u;
   uint32_t voff_w[WC], voff_x[XC];

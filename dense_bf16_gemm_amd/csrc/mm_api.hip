@@ -909,7 +909,7 @@ constexpr int64_t kSkinnyCUs = 256;  // workgroups resident at once: one per CU 
 
 bool skinny_shape(const Request& r) {
   return a_kcontig(r.layout) && b_kcontig(r.layout) && !r.ffn && !r.out_pre && r.batch == 1 &&
-         r.M <= mmk::kSkinnyMaxM && r.K >= 256 && r.K <= (int64_t(1) << 24) && r.N * r.K >= (int64_t(1) << 22);
+         r.M <= mmk::kSkinnyMaxM && r.K >= 256 && r.K <= (int64_t(1) << 23) && r.N * r.K >= (int64_t(1) << 22);
 }
 
 struct SkinnyPlan {

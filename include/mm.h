@@ -253,7 +253,7 @@ mm_status mm_set_config(const char* spec);
  * a call given a workspace (mm_matmul_ws, mm_linear_ws, mm_matmul_noalloc)
  * runs the slab kernel on 256 x <tile width> tiles instead.  Products of at
  * most 32 rows against at least 8 MiB of weights (layout MM_NT, one weight,
- * no forced configuration, K at most 2^24) name gemm_skinny, with
+ * no forced configuration, K at most 2^23) name gemm_skinny, with
  * SPLIT=<k slices>x32 (32 weight rows per workgroup) when a workspace would
  * cut K (no device query).  K = 0 names empty_k_fill.  form: 0 matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE
  * for bad args. */

@@ -171,12 +171,12 @@ def test_skinny_choices():
     assert binding.describe_config("linear", 17, 8192, 8192).endswith("KERNEL=gemm_skinny")
     assert binding.describe_config("linear", 32, 14336, 4096).endswith("KERNEL=gemm_skinny")
     # 33 rows, stored-[K][N] weights, an FFN pair, too little weight, K past
-    # 2^24: the tile kernels
+    # 2^23: the tile kernels
     assert not binding.describe_config("linear", 33, 8192, 8192).endswith("gemm_skinny")
     assert not binding.describe_config("matmul", 16, 8192, 8192, "nn").endswith("gemm_skinny")
     assert not binding.describe_config("ffn", 16, 8192, 8192).endswith("gemm_skinny")
     assert not binding.describe_config("linear", 16, 1024, 2048).endswith("gemm_skinny")
-    assert not binding.describe_config("linear", 1, 8, (1 << 24) + 8).endswith("gemm_skinny")
+    assert not binding.describe_config("linear", 1, 8, (1 << 23) + 8).endswith("gemm_skinny")
     assert binding.workspace_size("linear", 16, 14336, 4096) == 0
     assert binding.workspace_size("linear", 16, 8192, 8192) == 2 * 16 * 8192 * 4
 
