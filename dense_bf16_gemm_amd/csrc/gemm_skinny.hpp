@@ -30,8 +30,8 @@
 // (faster at 14336 x 4096, 6 us slower at 8192 x 8192).  Rows 17-32 (two
 // activation blocks, 48 KiB stages): 24 x 8192 x 8192 49.0 -> 35.9 us and
 // 32 x 14336 x 4096 47.7 -> 30.9 against the tile kernels (BLAS 30.0, 26.2),
-// but 32 x 28672 x 8192 106.6 -> 114.4.  Four blocks (64 rows, two 64 KiB
-// stages) lost to the tile kernels: 64 x 28672 x 8192 112.9 -> 134.3 us.
+// 32 x 28672 x 8192 106.6 -> 102.3 (112.6).  Four blocks (64 rows, two 64
+// KiB stages) lost to the tile kernels: 64 x 28672 x 8192 112.9 -> 134.3 us.
 #pragma once
 
 #include "gemm_kernel.hpp"

@@ -918,26 +918,32 @@ struct SkinnyPlan {
 };
 
 // The number of slices S (at most max_slices) that minimises the modelled
-// time: rounds of resident workgroups times the stages each streams, plus,
-// when split, the second launch (about as long as streaming 12.5 MB) and
-// the partial sums' traffic, in units of one round of stages (256
-// workgroups' stage of weights).
+// time, in bytes streamed at the full rate: the weight, slowed in proportion
+// when fewer workgroups are resident than it takes to keep HBM busy (128 +
+// 8 per activation row, at most 256: each row's copies slow a workgroup's
+// stream), plus, when split, the second launch (about as long as streaming
+// 18 MB) and the partial sums written and read back.  Measured with cold
+// weights: one row at 8192 x 8192 runs best unsplit (30.9 us against 33.9
+// in two slices), 16 rows at 4096 x 14336 in four slices (25.9 against 31.5
+// in two).
 SkinnyPlan skinny_plan(const Request& r, int64_t max_slices) {
   const int xb = mmk::skinny_xb((int)r.M);
-  const int64_t rows = mmk::skinny_rows(xb), kd = mmk::skinny_kd(xb);
+  const int64_t rows = mmk::skinny_rows(xb);
   const int64_t ngroups = cdiv(r.N, rows);
+  const double busy = (double)std::min<int64_t>(256, 128 + 8 * r.M);
+  const double wbytes = 2.0 * (double)r.N * (double)r.K;
   // one slice (no workspace) is always possible
   const int64_t smax =
-      std::max<int64_t>(1, std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, r.K / kd}));
+      std::max<int64_t>(1, std::min<int64_t>({mmk::kSkinnyMaxSlices, max_slices, r.K / mmk::skinny_kd(xb)}));
   SkinnyPlan sp;
   double best = -1.0;
   for (int64_t S = 1; S <= smax; ++S) {
     const int64_t kc = cdiv(cdiv(r.K, S), 64) * 64;
     const int64_t slices = cdiv(r.K, kc);
     if (slices != S) continue;
-    double cost = (double)cdiv(ngroups * slices, kSkinnyCUs) * (double)kc / (double)kd;
-    if (slices > 1)
-      cost += (12.5e6 + 2.0 * (double)(slices * r.M * r.N * 4)) / (kSkinnyCUs * 2.0 * (double)(rows * kd));
+    const double resident = (double)std::min<int64_t>(ngroups * slices, kSkinnyCUs);
+    double cost = wbytes * std::max(1.0, busy / resident);
+    if (slices > 1) cost += 18e6 + 2.0 * (double)(slices * r.M * r.N * 4);
     if (best < 0.0 || cost < best - 1e-9) {
       best = cost;
       sp.kc = (int)kc;
