@@ -255,27 +255,28 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
 // four consecutive outputs (one 16-byte load per slice when M*N is a
 // multiple of 4).
 __global__ void __launch_bounds__(256) skinny_reduce(SkinnyParams p) {
-  const int mn = p.M * p.N;
-  const int i = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 4;
+  // 64-bit positions: M * N may pass 2^31 (32 rows of a vocabulary-sized N)
+  const int64_t mn = (int64_t)p.M * p.N;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= mn) return;
   if ((mn & 3) == 0) {
     // every slice's load issued before the first add: one memory latency
     f32x4 w[kSkinnyMaxSlices];
 #pragma unroll
     for (int s = 0; s < kSkinnyMaxSlices; ++s)
-      if (s < p.slices) w[s] = *reinterpret_cast<const f32x4*>(p.part + (int64_t)s * mn + i);
+      if (s < p.slices) w[s] = *reinterpret_cast<const f32x4*>(p.part + s * mn + i);
     f32x4 v = w[0];
 #pragma unroll
     for (int s = 1; s < kSkinnyMaxSlices; ++s)
       if (s < p.slices) v = f32x4{v[0] + w[s][0], v[1] + w[s][1], v[2] + w[s][2], v[3] + w[s][3]};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) skinny_store(p, (i + e) / p.N, (i + e) % p.N, v[e]);
+    for (int e = 0; e < 4; ++e) skinny_store(p, (int)((i + e) / p.N), (int)((i + e) % p.N), v[e]);
     return;
   }
   for (int e = 0; e < 4 && i + e < mn; ++e) {
     float v = p.part[i + e];
-    for (int s = 1; s < p.slices; ++s) v += p.part[(int64_t)s * mn + i + e];
-    skinny_store(p, (i + e) / p.N, (i + e) % p.N, v);
+    for (int s = 1; s < p.slices; ++s) v += p.part[s * mn + i + e];
+    skinny_store(p, (int)((i + e) / p.N), (int)((i + e) % p.N), v);
   }
 }
 
