@@ -202,6 +202,20 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
   for (int i = 0; i < NS - 1; ++i)
     if (i < nst) copy_stage(i);
   for (int st = 0; st < nst; ++st) {
+#ifdef MM_DEBUG_FULL_SYNC
+    // race-check build: every copy drained before the stage is read, and
+    // every wave past its reads before the next copy is issued
+    skinny_wait<kCopies, 0>(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    compute(st);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nst) copy_stage(st + NS - 1);
+#else
     // stage st's copies are done when at most those of the stages after it
     // remain (a plain barrier: a fence here would wait for every copy)
     skinny_wait<kCopies, NS - 2>(min(NS - 2, nst - 1 - st));
@@ -210,6 +224,7 @@ __global__ void __launch_bounds__(256) gemm_skinny(SkinnyParams p) {
     asm volatile("" ::: "memory");
     if (st + NS - 1 < nst) copy_stage(st + NS - 1);
     compute(st);
+#endif
   }
 
   // the waves' k parts meet in LDS: waves 1..3 store, wave 0 adds in order

@@ -9,7 +9,9 @@ missing write-after-read synchronisation in the pipelined K loop: PR
 "Translate MmaOp patterns properly on Hopper", commit list.)  The cases cover
 every slab instance: the four operand storages, the FFN fusion, the second
 (pre-activation) output, chunk-major and stream-K split-K, and grids small
-enough that the ring runs on across several tiles per workgroup.
+enough that the ring runs on across several tiles per workgroup; and the
+skinny kernel's LDS ring (one and two activation blocks, unsplit and in
+slices).
 """
 import ctypes
 
@@ -229,3 +231,25 @@ def test_ffn_ragged_k(libs, grid):
     assert_same(run_both(libs, cfg, lambda lib: binding.check(lib.mm_ffn_swiglu(
         x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), out.data_ptr(), M, N, K, stream()),
         "mm_ffn_swiglu"), [out]))
+
+
+@pytest.mark.parametrize("case", [(16, 4104, 2056, True), (7, 1000, 8200, False), (7, 1000, 8200, True),
+                                  (29, 2056, 4104, True), (32, 8192, 1032, False)])
+def test_skinny(libs, case):
+    """The skinny kernel's ring of LDS stages: the race-check build drains
+    every copy before a stage is read and waits for every wave before the
+    next copy is issued."""
+    dev = torch.device("cuda:0")
+    M, N, K, ws = case
+    assert binding.describe_config("linear", M, N, K).endswith("KERNEL=gemm_skinny")
+    A, B = operands(M, N, K, "nt", 990 + M, dev)
+    bias = synth.randn_bf16((N,), 1.0, 991).to(dev)
+    nbytes = binding.workspace_size("linear", M, N, K) if ws else 0
+    assert nbytes > 0 or not ws, "this shape should be cut into slices"
+    wsp = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    say("skinny", (M, N, K), "ws" if ws else "no ws", nbytes)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert_same(run_both(libs, None, lambda lib: binding.check(lib.mm_linear_ws(
+        A.data_ptr(), B.data_ptr(), bias.data_ptr(), out.data_ptr(), M, N, K, binding.LAYOUTS["nt"],
+        binding.EPILOGUES["bias_gelu_tanh"], wsp.data_ptr() if ws else None, nbytes, stream()),
+        "mm_linear_ws"), [out]))
