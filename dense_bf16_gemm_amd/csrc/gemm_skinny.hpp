@@ -10,10 +10,10 @@
 // memory into LDS (buffer loads to LDS: no registers), the 16 or 32
 // activation rows of the stage come the same way, and the four waves each
 // multiply a quarter of the stage's k-steps with MFMAs whose fragments are
-// read from LDS; the waves' parts meet in LDS in a fixed order at the end.  With a
-// workspace K may also be cut into S slices (when that fills the CUs
-// better): each writes its fp32 sums to slice s of the workspace and
-// skinny_reduce adds the slices in k order.  Results: fp32 sums of the bf16
+// read from LDS; the waves' parts meet in LDS in a fixed order at the end.
+// With a workspace K may also be cut into S slices (when the workgroups
+// would not keep HBM busy otherwise): each writes its fp32 sums to slice s
+// of the workspace and skinny_reduce adds the slices in k order.  Results: fp32 sums of the bf16
 // products, the epilogue on the sum, one rounding -- the contraction and
 // epilogue of the other kernels.
 //
@@ -46,7 +46,7 @@ struct SkinnyParams {
   void* out;             // [M][N], bf16 or fp32
   float* part;           // [S][M][N] fp32 partial sums (S > 1), else null
   int M, N, K;
-  int kc;      // k per workgroup slice (a multiple of 32); the last may be shorter
+  int kc;      // k per workgroup slice (a multiple of 64); the last may be shorter
   int slices;  // S
   int epi;
   int out_f32;

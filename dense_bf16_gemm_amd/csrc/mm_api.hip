@@ -901,9 +901,9 @@ mm_status run_empty_k(const Request& r, void* stream) {
 // ----------------------------------------------------------------------------
 // Skinny products (gemm_skinny): K-contiguous single-weight single-output
 // products of at most 32 rows against at least 8 MiB of weights, unless a
-// configuration is forced.  Without a workspace each block of 32 weight rows
+// configuration is forced.  Without a workspace each block of 64 weight rows
 // is one workgroup; with one, K may also be cut into S slices (at most 16, of
-// at least one 512-k stage each) when that fills the CUs better.
+// at least one 256-k stage each) where the workgroups would not keep HBM busy.
 // ----------------------------------------------------------------------------
 constexpr int64_t kSkinnyCUs = 256;  // workgroups resident at once: one per CU (LDS)
 
