@@ -255,8 +255,8 @@ mm_status mm_set_config(const char* spec);
  * most 32 rows against at least 8 MiB of weights (layout MM_NT, one weight,
  * no forced configuration, K at most 2^23) name gemm_skinny, with
  * SPLIT=<k slices>x64 (64 weight rows per workgroup) when a workspace would
- * cut K (no device query).  K = 0 names empty_k_fill.  form: 0 matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE
- * for bad args. */
+ * cut K (no device query).  K = 0 names empty_k_fill.  form: 0
+ * matmul/linear, 1 FFN.  Returns MM_ERR_INVALID_VALUE for bad args. */
 mm_status mm_describe_config(int form, int64_t M, int64_t N, int64_t K, mm_layout layout,
                              char* buf, int64_t buflen);
 
